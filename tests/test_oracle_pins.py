@@ -1,0 +1,432 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Page: "A Fused Hadamard + NVFP4 Quantization Kernel in Triton" (kanthi.in).
+Every test here runs on the CPU.  None of them compares the oracle with
+itself: each one checks it against a printed value, a closed form, an
+invariant, a library routine on a special case, an exhaustive nearest-point
+search, or an exact-rational re-implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_model as em
+import oracle
+import synth
+from conftest import read_golden
+
+F32 = np.float32
+
+
+def sylvester16() -> np.ndarray:
+    """H16 built by Kronecker doubling [[H, H], [H, -H]] four times, then /4
+    (section 2, hadamard16)."""
+    h = np.ones((1, 1))
+    for _ in range(4):
+        h = np.block([[h, h], [h, -h]])
+    return h / 4.0
+
+
+# ---------------------------------------------------------------- P1: rotation
+
+def test_rotation_columns_are_sylvester():
+    """The butterfly applied to each unit vector gives that column of H16, exactly."""
+    H = sylvester16().astype(np.float32)
+    for i in range(16):
+        e = np.zeros(16, dtype=np.float32)
+        e[i] = 1.0
+        y = oracle.rotate16(e)
+        assert np.array_equal(y, H[:, i]), i
+
+
+def test_rotation_is_orthonormal_exactly():
+    """Section 1: H*H^T = I; exact in binary32 (entries +-1/4, sums of 16)."""
+    cols = np.stack([oracle.rotate16(np.eye(16, dtype=np.float32)[i]) for i in range(16)], 1)
+    prod = cols.astype(np.float32) @ cols.T.astype(np.float32)
+    assert np.array_equal(prod, np.eye(16, dtype=np.float32))
+
+
+def test_rotation_is_an_involution_on_small_integers():
+    """H16 is symmetric and orthonormal, so H(Hx) = x; exact for small integers."""
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        x = rng.integers(-100, 101, 16).astype(np.float32)
+        assert np.array_equal(oracle.rotate16(oracle.rotate16(x)), x)
+
+
+def test_rotation_within_rounding_bound_of_fp64():
+    """|y_bfly - (H x)_fp64| <= gamma_5 * sum|x| / 4 (four rounded additions and
+    one rounded scaling along each path), plus Parseval."""
+    H = sylvester16()
+    rng = np.random.default_rng(2)
+    u = 2.0 ** -24
+    gamma5 = 5 * u / (1 - 5 * u)
+    for _ in range(2000):
+        x = (rng.standard_normal(16) * np.exp(rng.normal(0, 3, 16))).astype(np.float32)
+        y = oracle.rotate16(x).astype(np.float64)
+        yref = H @ x.astype(np.float64)
+        bound = gamma5 * np.abs(x.astype(np.float64)).sum() / 4.0 + 1e-300
+        assert np.all(np.abs(y - yref) <= bound)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(x.astype(np.float64))) <= \
+            1e-5 * np.linalg.norm(x.astype(np.float64))
+
+
+def test_rotation_stage_order_is_ascending():
+    """Reading: strides 1, 2, 4, 8 in that order.  The exact-rational model
+    follows that order; a vector where the order changes the binary32 result
+    shows the pin is sensitive to it."""
+    x = np.array([1.0, 2.0 ** -24, 2.0 ** -24, 0, 2.0 ** -24, 0, 0, 0,
+                  0, 0, 0, 0, 0, 0, 0, 2.0 ** -25], dtype=np.float32)
+    model = [em.frac_to_f32(v) for v in em.rotate16([em.f32_to_frac(v) for v in x])]
+    assert np.array_equal(oracle.rotate16(x), np.array(model, dtype=np.float32))
+    # the same stages in descending order give different bits for this vector
+    z = [em.f32_to_frac(v) for v in x]
+    h = 8
+    while h >= 1:
+        for i in range(16):
+            if i & h == 0:
+                a, b = z[i], z[i + h]
+                z[i], z[i + h] = em.rn32(a + b), em.rn32(a - b)
+        h //= 2
+    desc = np.array([em.frac_to_f32(em.rn32(v / 4)) for v in z], dtype=np.float32)
+    assert not np.array_equal(desc, oracle.rotate16(x))
+
+
+# ---------------------------------------------------------------- P2: E2M1
+
+def test_e2m1_table_from_the_page():
+    for value, code in read_golden("e2m1_table.txt"):
+        v = float(value)
+        if value == "-0.0":
+            v = -0.0
+        assert oracle.e2m1_code(v) == int(code), value
+
+
+def test_e2m1_neighbours_of_every_midpoint():
+    """One ulp either side of each midpoint falls on the nearer grid point."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for k, m in enumerate(mids):
+        below = np.nextafter(F32(m), F32(0))
+        above = np.nextafter(F32(m), F32(np.inf))
+        assert oracle.e2m1_code(below) == k, m
+        assert oracle.e2m1_code(above) == k + 1, m
+        assert oracle.e2m1_code(-below) == k + 8, m
+        assert oracle.e2m1_code(-above) == k + 9, m
+
+
+def test_e2m1_exhaustive_against_nearest_point(sweeps_lib):
+    """All 2^32 - 2^24 non-NaN binary32 inputs against a nearest-grid search."""
+    first = ctypes.c_uint32(0)
+    bad = sweeps_lib.sweep_e2m1_all(ctypes.byref(first))
+    assert bad == 0, f"{bad} mismatches, first at bits {first.value:#010x}"
+
+
+# ---------------------------------------------------------------- P3: E4M3
+
+def test_e4m3_worked_values_from_the_page():
+    for inp, rne, faulty in read_golden("e4m3_worked_values.txt"):
+        b = oracle.e4m3_byte(float(inp))
+        assert oracle.e4m3_value(b) == float(rne), inp
+        if float(faulty) != float(rne):
+            assert oracle.e4m3_value(b) != float(faulty)
+
+
+def test_e4m3_anchor_bytes():
+    for value, byte in read_golden("e4m3_anchors.txt"):
+        assert oracle.e4m3_byte(float(value)) == int(byte, 16), value
+        assert oracle.e4m3_value(int(byte, 16)) == float(value), value
+
+
+def test_e4m3_saturates_at_448():
+    for v in (448.0, 449.0, 463.9, 464.0, 465.0, 480.0, 1e6, 3.0e38, float("inf")):
+        assert oracle.e4m3_byte(v) == 0x7E, v
+
+
+def test_e4m3_ties_go_to_even():
+    # 1.0625 sits halfway between 1.0 (mantissa 0) and 1.125 (mantissa 1)
+    assert oracle.e4m3_value(oracle.e4m3_byte(1.0625)) == 1.0
+    # 1.1875 halfway between 1.125 (odd) and 1.25 (even)
+    assert oracle.e4m3_value(oracle.e4m3_byte(1.1875)) == 1.25
+    # 2^-10 halfway between 0 and 2^-9: goes to 0; 3*2^-10 goes to 2^-8
+    assert oracle.e4m3_byte(2.0 ** -10) == 0
+    assert oracle.e4m3_value(oracle.e4m3_byte(3 * 2.0 ** -10)) == 2.0 ** -8
+
+
+def test_e4m3_exhaustive_against_nearest_point(sweeps_lib):
+    """Every binary32 in [0, 2^10] (and up to +inf) against a bisection
+    nearest-value search over the 127 E4M3 values."""
+    first = ctypes.c_uint32(0)
+    bad = sweeps_lib.sweep_e4m3_range(0, 0x7F800000, ctypes.byref(first))
+    assert bad == 0, f"{bad} mismatches, first at bits {first.value:#010x}"
+
+
+def test_e4m3_strided_against_linear_search(sweeps_lib):
+    first = ctypes.c_uint32(0)
+    bad = sweeps_lib.sweep_e4m3_linear(0, 0x44800000, 97, ctypes.byref(first))
+    assert bad == 0, f"{bad} mismatches, first at bits {first.value:#010x}"
+
+
+def test_e4m3_exhaustive_against_torch_cast():
+    """PyTorch's float8_e4m3fn cast (round to nearest even; the reference cast
+    of section 3) on every binary32 in [0, 464); above that torch gives NaN and
+    the definition clamps at 448."""
+    hi = int(np.float32(464.0).view(np.uint32))
+    step = 1 << 25
+    for lo in range(0, hi, step):
+        n = min(step, hi - lo)
+        bits = np.arange(lo, lo + n, dtype=np.uint32)
+        vals = bits.view(np.float32)
+        ours = oracle.e4m3_bytes(vals)
+        ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        mism = np.nonzero(ours != ref)[0]
+        assert mism.size == 0, f"first mismatch at bits {bits[mism[0]]:#010x}"
+
+
+# ---------------------------------------------------------------- P4-P6: scales and sizes
+
+def _bf16(x: np.ndarray) -> np.ndarray:
+    return synth.round_bf16(np.asarray(x, dtype=np.float64))
+
+
+def test_all_zero_tensor():
+    x = np.zeros((4, 64), dtype=np.uint16)
+    for rotate in (True, False):
+        q, s, g, a = oracle.quantize(x, rotate)
+        assert g == 1.0 and a == 0.0
+        assert not q.any() and not s.any()
+
+
+def test_largest_block_scale_is_448():
+    """The global scale puts the block holding the global amax at 448 (0x7E)."""
+    for seed in range(6):
+        x = synth.normal_bf16(64 * 256, seed=seed, scale=10.0 ** (seed - 3)).reshape(64, 256)
+        for rotate in (True, False):
+            q, s, g, a = oracle.quantize(x, rotate)
+            assert s.max() == 0x7E
+            assert g > 0 and abs(float(g) * 2688.0 - float(a)) <= 4e-7 * float(a)
+
+
+def test_full_scale_blocks_reach_code_7():
+    """Invariant: a block with a normal-range E4M3 scale below 448 has its
+    largest element at code 7, since a_b / (s g) lies in (5, 6.4]."""
+    w = synth.make("gauss_1pct_cols_4096x4096", rows=64)
+    for rotate in (True, False):
+        q, s, g, a = oracle.quantize(w.x, rotate)
+        codes = np.stack([q & 15, q >> 4], -1).reshape(s.shape[0], -1, 16)
+        mag = (codes & 7).max(-1)
+        scale_vals = np.vectorize(oracle.e4m3_value)(s)
+        normal = (scale_vals >= 2.0 ** -6)
+        assert normal.any()
+        assert np.all(mag[normal] == 7)
+
+
+def test_storage_is_4p5_bits_per_value():
+    rows = dict(read_golden("format_sizes.txt"))
+    x = synth.normal_bf16(256 * 64, seed=3).reshape(256, 64)
+    q, s, g, a = oracle.quantize(x, True)
+    assert q.size == int(rows["packed_bytes"]) and s.size == int(rows["scale_bytes"])
+    assert (q.size + s.size) / x.size == float(rows["bytes_per_value"])
+
+
+# ---------------------------------------------------------------- P7: exact-rational model
+
+def _tiny_inputs(n_cases: int):
+    """Small tensors mixing magnitudes so that butterfly sums round, scales land
+    near E4M3 midpoints and quotients near E2M1 midpoints."""
+    rng = np.random.default_rng(7)
+    for i in range(n_cases):
+        rows = int(rng.integers(1, 4))
+        cols = 16 * int(rng.integers(1, 4))
+        n = rows * cols
+        kind = i % 5
+        if kind == 0:
+            v = rng.standard_normal(n)
+        elif kind == 1:
+            v = rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))
+        elif kind == 2:
+            v = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], n) * \
+                rng.choice([-1.0, 1.0], n)
+        elif kind == 3:
+            v = rng.integers(-64, 65, n).astype(np.float64) / 8.0
+        else:
+            v = rng.standard_normal(n)
+            v[rng.integers(0, n, max(1, n // 8))] = 0.0
+            v[rng.integers(0, n)] *= 1e4
+        f32 = (i % 2 == 1)
+        if f32:
+            x = v.astype(np.float32).reshape(rows, cols)
+            xf = x
+        else:
+            x = _bf16(v).reshape(rows, cols)
+            xf = synth.bf16_to_f32(x)
+        yield x, xf, bool(rng.integers(0, 2))
+
+
+def test_oracle_matches_exact_rational_model():
+    n = 0
+    for x, xf, rotate in _tiny_inputs(1500):
+        q, s, g, a = oracle.quantize(x, rotate)
+        mq, ms, mg, ma = em.quantize(xf, rotate)
+        assert np.array_equal(q, mq), (x, rotate)
+        assert np.array_equal(s, ms), (x, rotate)
+        assert em.f32_bits(g) == em.f32_bits(mg) and em.f32_bits(a) == em.f32_bits(ma)
+        n += 1
+    assert n == 1500
+
+
+def test_divisor_one_when_scale_rounds_to_zero():
+    """When a block's scale rounds to E4M3 zero the divisor is 1.0 and codes
+    come from the raw values (section 2, the where(s_f == 0, 1, s_f) guard)."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 2.0 ** 20          # block 0 sets amax = 2^20, g = 2^20 / 2688
+    x[0, 16:] = 0.3              # block 1: (0.3/6)/g < 2^-10, so s rounds to 0
+    q, s, g, a = oracle.quantize(x, False)
+    assert s[0, 0] == 0x7E and s[0, 1] == 0
+    assert np.all((q[0, 8:] & 15) == 1) and np.all((q[0, 8:] >> 4) == 1)
+    mq, ms, mg, ma = em.quantize(x, False)
+    assert np.array_equal(q, mq) and np.array_equal(s, ms)
+
+
+def test_sign_of_zero_and_tiny_negatives():
+    """Code 8 needs a quotient below zero; -0.0 gives code 0 (section 2: sign
+    bit from v < 0)."""
+    x = np.zeros((1, 16), dtype=np.float32)
+    x[0, 0] = 6.0
+    x[0, 1] = -0.0
+    x[0, 2] = -1e-30
+    x[0, 3] = 1e-30
+    q, s, g, a = oracle.quantize(x, False)
+    codes = np.stack([q & 15, q >> 4], -1).reshape(-1)
+    assert codes[0] == 7 and codes[1] == 0 and codes[2] == 8 and codes[3] == 0
+
+
+# ---------------------------------------------------------------- P8: printed errors
+
+def _page_tensors():
+    torch.manual_seed(0)
+    x = torch.randn(256, 64)
+    x[:, [3, 17, 40]] *= 20.0
+    gauss = torch.randn(256, 64)
+    t3 = torch.distributions.StudentT(3.0).sample((256, 64))
+    return x.numpy().copy(), gauss.numpy().copy(), t3.numpy().copy()
+
+
+def test_printed_round_trip_errors():
+    """Sections 3 and 5 print eight relative L2 errors to four decimals."""
+    expected = {r[0]: (float(r[1]), float(r[2])) for r in read_golden("error_table.txt")}
+    x, gauss, t3 = _page_tensors()
+    normal_cols = np.ones(64, dtype=np.uint8)
+    normal_cols[[3, 17, 40]] = 0
+    cases = {"outlier_all": (x, None), "outlier_normal": (x, normal_cols),
+             "gaussian": (gauss, None), "student_t3": (t3, None)}
+    for name, (t, mask) in cases.items():
+        got = []
+        for rotate in (False, True):
+            q, s, g, a = oracle.quantize(np.ascontiguousarray(t, dtype=np.float32), rotate)
+            got.append(oracle.roundtrip_error(t, rotate, q, s, g, mask))
+        assert round(got[0], 4) == expected[name][0], (name, got)
+        assert round(got[1], 4) == expected[name][1], (name, got)
+
+
+# ---------------------------------------------------------------- P9: thread-count invariance
+
+def test_thread_count_does_not_change_bytes():
+    w = synth.make("t3_lognormal_16384x8192", rows=64)
+    r1 = oracle.quantize(w.x, True, nthreads=1)
+    r8 = oracle.quantize(w.x, True, nthreads=8)
+    for a, b in zip(r1, r8):
+        assert np.array_equal(np.asarray(a), np.asarray(b))
+
+
+# ---------------------------------------------------------------- P10: library special case
+
+def torch_reference(xf: torch.Tensor, rotate: bool):
+    """The arithmetic of section 3's reference in PyTorch (CPU, fp32): a dense
+    matmul rotation, torch's float8_e4m3fn cast for the scales, IEEE division,
+    the seven threshold compares.  With rotate=False nothing is summed, so this
+    computes exactly the definition with library routines."""
+    y = xf.reshape(-1, 16).float()
+    if rotate:
+        y = y @ torch.from_numpy(sylvester16().astype(np.float32))
+    g = float(y.abs().max() / 6.0 / 448.0) or 1.0
+    s = (y.abs().amax(1) / 6.0 / g).to(torch.float8_e4m3fn)
+    sf = s.float() * g
+    v = y / torch.where(sf == 0, torch.ones_like(sf), sf)[:, None]
+    a = v.abs()
+    c = ((a > 0.25).int() + (a >= 0.75).int() + (a > 1.25).int() + (a >= 1.75).int()
+         + (a > 2.5).int() + (a >= 3.5).int() + (a > 5.0).int())
+    c = (c + (v < 0).int() * 8).to(torch.uint8)
+    q = c[:, 0::2] | (c[:, 1::2] << 4)
+    return q.numpy(), s.view(torch.uint8).numpy(), np.float32(g)
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("gauss_outliers_128x1024", None),
+    ("gauss_1pct_cols_4096x4096", 512),
+    ("silu_ties_32768x14336", 128),
+    ("kv_heads_65536x8x128_f32", 256),
+    ("t3_lognormal_16384x8192", 128),
+])
+def test_rotate_off_equals_torch_reference(name, rows):
+    w = synth.make(name, rotate=False, rows=rows)
+    xf = synth.bf16_to_f32(w.x) if w.dtype == "bf16" else w.x
+    q, s, g, a = oracle.quantize(w.x, False)
+    rq, rs, rg = torch_reference(torch.from_numpy(xf.copy()), False)
+    assert em.f32_bits(g) == em.f32_bits(rg)
+    assert np.array_equal(s.reshape(-1), rs.reshape(-1))
+    assert np.array_equal(q.reshape(-1, 8), rq)
+
+
+def test_rotate_on_close_to_torch_reference():
+    """With the rotation, the page's reference sums in the matmul's order, so
+    bits may differ where a sum rounds; on bf16 data that is rare."""
+    w = synth.make("gauss_1pct_cols_4096x4096", rows=256)
+    xf = synth.bf16_to_f32(w.x)
+    q, s, g, a = oracle.quantize(w.x, True)
+    rq, rs, rg = torch_reference(torch.from_numpy(xf.copy()), True)
+    assert np.mean(q.reshape(-1, 8) != rq) < 1e-4
+    assert np.mean(s.reshape(-1) != rs.reshape(-1)) < 1e-4
+
+
+def test_page_demo_tensor_matches_reference_codes():
+    """Section 3: codes and scales of the demo tensor match the reference,
+    with and without the rotation."""
+    x, _, _ = _page_tensors()
+    for rotate in (False, True):
+        q, s, g, a = oracle.quantize(x, rotate)
+        rq, rs, rg = torch_reference(torch.from_numpy(x), rotate)
+        assert np.array_equal(q.reshape(-1, 8), rq)
+        assert np.array_equal(s.reshape(-1), rs.reshape(-1))
+
+
+# ---------------------------------------------------------------- P11: the halved-scale trap
+
+def test_no_block_scale_is_halved():
+    """Section 4: a lost exponent carry halves a scale; the oracle's scales
+    equal torch's cast of the same values and none is half of it."""
+    x, _, _ = _page_tensors()
+    q, s, g, a = oracle.quantize(x, False)
+    _, rs, _ = torch_reference(torch.from_numpy(x), False)
+    ours = np.vectorize(oracle.e4m3_value)(s.reshape(-1))
+    ref = np.vectorize(oracle.e4m3_value)(rs.reshape(-1))
+    assert not np.any((ref > 0) & (ours == ref / 2))
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------- dequant in fp64
+
+def test_dequant_inverts_exactly_representable_blocks():
+    """A block whose rotated values sit on the E2M1 grid times a power-of-two
+    scale decodes back to the input exactly (fp64 decode, exact H)."""
+    t = np.array([6, -4, 3, 2, -1.5, 1, 0.5, 0, -6, 4, -3, 2, 1.5, -1, 0.5, 0],
+                 dtype=np.float64)
+    H = sylvester16()
+    x = (H @ t).astype(np.float32).reshape(1, 16)   # exact: multiples of 1/8
+    q, s, g, a = oracle.quantize(x, True)
+    back = oracle.dequant_f64(q, s, g, True)
+    assert np.array_equal(back.reshape(-1), x.astype(np.float64).reshape(-1))

@@ -1,0 +1,149 @@
+/*
+ * nvfp4rq.h - fused block-Hadamard rotation + NVFP4 activation quantization
+ * on AMD Instinct MI355X (gfx950).  C ABI of libnvfp4rq.so.
+ *
+ * The method (page "A Fused Hadamard + NVFP4 Quantization Kernel in Triton",
+ * kanthi.in):
+ *   - section 1 "The format, precisely": x ~ q * s_block * s_global with q an
+ *     E2M1 code per element, s_block one E4M3 byte per 16 consecutive values,
+ *     s_global one fp32 per tensor; the 16-element block is first rotated by
+ *     the orthonormal 16x16 Sylvester-Hadamard matrix (entries +-1/4);
+ *   - section 2 "The kernel": s_global = rotated global amax / 6 / 448
+ *     (1.0 when that is zero); s_block = (block amax / 6) / s_global rounded
+ *     to E4M3 and clamped at 448; each rotated value divided by
+ *     float(s_block) * s_global (by 1.0 when that product is zero) becomes an
+ *     E2M1 code by midpoint compares with ties to the even code, sign in bit
+ *     3; two codes per byte, even element in the low nibble;
+ *   - section 3 "Bit-exact against a reference": E4M3 rounding is to nearest,
+ *     ties to even.
+ * The stored layout matches the page "NVFP4 Quantization" (atlas-docs),
+ * section "The numeric format": codes [rows, cols/2], scales [rows, cols/16]
+ * along K (the column axis).
+ *
+ * Arithmetic contract (bit-exact, reproducible across launch shapes): every
+ * step is binary32 with round-to-nearest-even and gradual underflow; the
+ * rotation is the butterfly with strides 1, 2, 4, 8 (pairs (a+b, a-b)) then a
+ * multiply by 0.25; s_global = (amax / 6) / 448 and the block value
+ * (block_amax / 6) / s_global are each two correctly rounded divisions; the
+ * element quotient is one correctly rounded division.  Inputs must be finite
+ * with |x| <= 2^123 (so that no sum of 16 values overflows); NaN or Inf input
+ * gives unspecified codes, and a NaN shows up in *amax_out as a NaN bit
+ * pattern.
+ *
+ * Common rules for every entry point:
+ *   - Pointers marked "device" must be device memory of the current HIP
+ *     device (or memory it can access).  The caller owns every buffer; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without waiting for it.  Nothing is read back to the host.
+ *   - Validation happens before anything is enqueued: a non-zero status means
+ *     no work was enqueued and no output was touched.  NVFP4_ERR_HIP means a
+ *     launch was rejected by the runtime; earlier launches of the same call
+ *     may already be enqueued.  Faults inside kernels surface at the caller's
+ *     next synchronisation, as usual for HIP.
+ *   - Outputs must not overlap the input or each other (NVFP4_ERR_ARG).
+ *   - Calls that share an amax/gscale buffer must be ordered (same stream or
+ *     explicit events): the amax buffer is an atomic accumulator.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef NVFP4RQ_H
+#define NVFP4RQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,  /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = 2, /* rows < 0, cols < 0, cols % 16 != 0, or the size overflows */
+    NVFP4_ERR_ALIGN = 3, /* a pointer misses the alignment its argument requires */
+    NVFP4_ERR_ARG = 4,   /* rotate not 0 or 1, overlapping buffers, or a bad scale */
+    NVFP4_ERR_HIP = 5    /* the HIP runtime rejected a launch */
+} nvfp4_status;
+
+/*
+ * Full path: rotated global amax (pass 1), global scale, then rotate+quantize
+ * every block (pass 2).  Page "A Fused Hadamard + NVFP4 Quantization Kernel in
+ * Triton", section 2 (quantize and hadamard_nvfp4_kernel), with the global amax
+ * computed on the device instead of on the host.
+ *
+ *   x_bf16      device, bf16 bit patterns, row-major contiguous [rows, cols],
+ *               16-byte aligned.  cols % 16 == 0.  May be NULL when
+ *               rows * cols == 0.
+ *   rows, cols  tensor shape; blocks are 16 consecutive values of a row.
+ *   rotate      1: rotate each block by H16 before scaling; 0: no rotation.
+ *   q_out       device, rows * cols / 2 bytes, 16-byte aligned: E2M1 codes,
+ *               row-major [rows, cols/2], element 2k in the low nibble of
+ *               byte k.  May be NULL when rows * cols == 0.
+ *   s_out       device, rows * cols / 16 bytes, 4-byte aligned: E4M3FN block
+ *               scales (0x00..0x7E), row-major [rows, cols/16].  May be NULL
+ *               when rows * cols == 0.
+ *   gscale_out  device, 1 float, 4-byte aligned: the global scale s_global.
+ *   amax_out    device, 1 float, 4-byte aligned: the rotated global amax.
+ *               Used as the pass-1 accumulator; zeroed by this call.
+ *   stream      HIP stream.
+ * rows * cols == 0 is valid: it writes amax 0 and global scale 1.
+ */
+nvfp4_status nvfp4_rotquant(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,
+                            uint8_t *q_out, uint8_t *s_out, float *gscale_out,
+                            float *amax_out, hipStream_t stream);
+
+/* As nvfp4_rotquant for fp32 input (x: device, float [rows, cols], 16-byte
+   aligned).  The page's own tests quantize fp32 activations (section 3). */
+nvfp4_status nvfp4_rotquant_f32(const float *x, int64_t rows, int64_t cols, int rotate,
+                                uint8_t *q_out, uint8_t *s_out, float *gscale_out,
+                                float *amax_out, hipStream_t stream);
+
+/*
+ * Pass 1 alone: *amax_out = max |y| over the whole tensor, y the rotated
+ * blocks (or the values themselves when rotate == 0).  Section 2 of the same
+ * page: the global scale needs the amax of the whole rotated tensor before any
+ * block can be scaled.  Arguments as nvfp4_rotquant.  The buffer is zeroed and
+ * then accumulated with one atomic maximum per workgroup.
+ */
+nvfp4_status nvfp4_rotamax(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,
+                           float *amax_out, hipStream_t stream);
+nvfp4_status nvfp4_rotamax_f32(const float *x, int64_t rows, int64_t cols, int rotate,
+                               float *amax_out, hipStream_t stream);
+
+/*
+ * Pass 2 alone: reads the amax from device memory (as written by
+ * nvfp4_rotamax), derives the global scale, writes it to *gscale_out and
+ * quantizes every block.  Section 2 of the same page (hadamard_nvfp4_kernel).
+ *   amax_in  device, 1 float, 4-byte aligned, finite and >= 0.
+ * Other arguments as nvfp4_rotquant.
+ */
+nvfp4_status nvfp4_quant_from_amax(const uint16_t *x_bf16, int64_t rows, int64_t cols,
+                                   int rotate, const float *amax_in, uint8_t *q_out,
+                                   uint8_t *s_out, float *gscale_out, hipStream_t stream);
+nvfp4_status nvfp4_quant_from_amax_f32(const float *x, int64_t rows, int64_t cols, int rotate,
+                                       const float *amax_in, uint8_t *q_out, uint8_t *s_out,
+                                       float *gscale_out, hipStream_t stream);
+
+/*
+ * Dequantize for round-trip checks (section 2, dequantize): each code becomes
+ * +-{0, .5, 1, 1.5, 2, 3, 4, 6}[code & 7] times fl(float(s) * gscale), rounded
+ * to binary32; when rotate == 1 the block is then multiplied by H16^T = H16
+ * with the same binary32 butterfly and the multiply by 0.25.
+ *   q       device, rows * cols / 2 bytes, 8-byte aligned (layout of q_out).
+ *   s       device, rows * cols / 16 bytes (layout of s_out).
+ *   gscale  device, 1 float, 4-byte aligned, > 0 and finite.
+ *   y_out   device, float [rows, cols], 16-byte aligned.
+ * Pointers other than gscale may be NULL when rows * cols == 0.
+ */
+nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gscale,
+                           int64_t rows, int64_t cols, int rotate, float *y_out,
+                           hipStream_t stream);
+
+/* Static English text for a status code; never NULL. */
+const char *nvfp4_status_string(nvfp4_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4RQ_H */

@@ -1,0 +1,162 @@
+"""Fused block-Hadamard rotation + NVFP4 activation quantization on MI355X.
+
+Thin ctypes binding over ``libnvfp4rq.so`` (HIP, gfx950), whose C ABI is
+declared in ``include/nvfp4rq.h``.  This module only marshals arguments: it
+allocates outputs with PyTorch on the input's device, takes the current HIP
+stream from PyTorch, and calls the library.  Every step of the method runs in
+the library's kernels; there is no fallback path, and importing this module
+fails if the library is not built.
+
+Method: page "A Fused Hadamard + NVFP4 Quantization Kernel in Triton",
+sections 1-3 (two-level NVFP4 scaling of 16-element blocks after a 16-point
+Hadamard rotation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "Nvfp4Error", "rotquant", "rotamax", "quant_from_amax", "dequant",
+    "status_string", "lib",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4rq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+_SIGS = {
+    "nvfp4_rotquant": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
+    "nvfp4_rotquant_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
+    "nvfp4_rotamax": [_p, _i64, _i64, _int, _p, _p],
+    "nvfp4_rotamax_f32": [_p, _i64, _i64, _int, _p, _p],
+    "nvfp4_quant_from_amax": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
+    "nvfp4_quant_from_amax_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
+    "nvfp4_dequant": [_p, _p, _p, _i64, _i64, _int, _p, _p],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _int
+lib.nvfp4_status_string.argtypes = [_int]
+lib.nvfp4_status_string.restype = ctypes.c_char_p
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return lib.nvfp4_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Nvfp4Error(fn, status)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr() or None
+
+
+def _stream(device: torch.device, stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _variant(x: torch.Tensor, base: str) -> str:
+    if x.dtype == torch.bfloat16:
+        return base
+    if x.dtype == torch.float32:
+        return base + "_f32"
+    raise TypeError(f"input must be bfloat16 or float32, got {x.dtype}")
+
+
+def _check_input(x: torch.Tensor) -> tuple[int, int]:
+    if x.dim() != 2:
+        raise ValueError("input must be 2-D [rows, cols]")
+    if not x.is_cuda:
+        raise ValueError("input must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError("input must be contiguous (row-major)")
+    return x.shape[0], x.shape[1]
+
+
+def rotamax(x: torch.Tensor, rotate: bool = True, amax: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """Pass 1: the rotated global amax, as a float32 device tensor [1]."""
+    rows, cols = _check_input(x)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    fn = _variant(x, "nvfp4_rotamax")
+    _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(amax),
+                                _stream(x.device, stream)))
+    return amax
+
+
+def quant_from_amax(x: torch.Tensor, amax: torch.Tensor, rotate: bool = True,
+                    out: tuple | None = None, stream=None):
+    """Pass 2: global scale from a device amax, then rotate+quantize.
+    Returns (q uint8 [rows, cols/2], s uint8 [rows, cols/16], g float32 [1])."""
+    rows, cols = _check_input(x)
+    if out is None:
+        q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+        s = torch.empty(rows, cols // 16, dtype=torch.uint8, device=x.device)
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        q, s, g = out
+    fn = _variant(x, "nvfp4_quant_from_amax")
+    _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(amax), _ptr(q),
+                                _ptr(s), _ptr(g), _stream(x.device, stream)))
+    return q, s, g
+
+
+def rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, stream=None):
+    """Both passes.  x: bfloat16 or float32 [rows, cols], cols % 16 == 0.
+    Returns (q uint8 [rows, cols/2], s uint8 [rows, cols/16] E4M3FN bytes,
+    g float32 [1] global scale, amax float32 [1])."""
+    rows, cols = _check_input(x)
+    if out is None:
+        q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+        s = torch.empty(rows, cols // 16, dtype=torch.uint8, device=x.device)
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+        a = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        q, s, g, a = out
+    fn = _variant(x, "nvfp4_rotquant")
+    _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(q), _ptr(s),
+                                _ptr(g), _ptr(a), _stream(x.device, stream)))
+    return q, s, g, a
+
+
+def dequant(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = True,
+            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode codes and scales back to float32 [rows, cols] (inverse rotation
+    included when rotate)."""
+    if s.dim() != 2 or q.dim() != 2:
+        raise ValueError("q and s must be 2-D")
+    rows, cols = s.shape[0], s.shape[1] * 16
+    if q.shape != (rows, cols // 2):
+        raise ValueError("q and s shapes disagree")
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.float32, device=q.device)
+    _check("nvfp4_dequant", lib.nvfp4_dequant(_ptr(q), _ptr(s), _ptr(g), rows, cols,
+                                              int(bool(rotate)), _ptr(out),
+                                              _stream(q.device, stream)))
+    return out

@@ -1,0 +1,127 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and rejects bad arguments before any HIP call (validation is host-only, so
+these calls never touch a device and run without a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "nvfp4rq.h")
+LIB = os.path.join(ROOT, "nvfp4_activation_amd", "libnvfp4rq.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ARG, ERR_HIP = range(6)
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    lib = ctypes.CDLL(LIB)
+    p, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    for name in ("nvfp4_rotquant", "nvfp4_rotquant_f32", "nvfp4_quant_from_amax",
+                 "nvfp4_quant_from_amax_f32"):
+        getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p]
+    for name in ("nvfp4_rotamax", "nvfp4_rotamax_f32"):
+        getattr(lib, name).argtypes = [p, i64, i64, i, p, p]
+    lib.nvfp4_dequant.argtypes = [p, p, p, i64, i64, i, p, p]
+    lib.nvfp4_status_string.argtypes = [i]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("nvfp4_rotquant", "nvfp4_rotquant_f32", "nvfp4_dequant",
+                 "nvfp4_status_string", "nvfp4_rotamax", "nvfp4_quant_from_amax"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    seen = set()
+    for st in range(6):
+        s = lib.nvfp4_status_string(st).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.nvfp4_status_string(99).decode() == "unknown status"
+
+
+# Fake, never-dereferenced device addresses: validation only looks at them.
+X, Q, S, G, A = 0x10000, 0x20000, 0x30000, 0x40000, 0x40010
+
+
+def rq(lib, x=X, rows=4, cols=64, rotate=1, q=Q, s=S, g=G, a=A, name="nvfp4_rotquant"):
+    if "from_amax" in name:   # (x, rows, cols, rotate, amax_in, q, s, gscale, stream)
+        return getattr(lib, name)(x, rows, cols, rotate, a, q, s, g, None)
+    return getattr(lib, name)(x, rows, cols, rotate, q, s, g, a, None)
+
+
+@pytest.mark.parametrize("name", ["nvfp4_rotquant", "nvfp4_rotquant_f32",
+                                  "nvfp4_quant_from_amax", "nvfp4_quant_from_amax_f32"])
+def test_quant_validation(lib, name):
+    f = lambda **kw: rq(lib, name=name, **kw)  # noqa: E731
+    assert f(x=None) == ERR_NULL
+    assert f(q=None) == ERR_NULL
+    assert f(s=None) == ERR_NULL
+    assert f(g=None) == ERR_NULL
+    assert f(a=None) == ERR_NULL
+    assert f(cols=24) == ERR_SHAPE
+    assert f(cols=-16) == ERR_SHAPE
+    assert f(rows=-1) == ERR_SHAPE
+    assert f(rows=1 << 40, cols=1 << 40) == ERR_SHAPE
+    assert f(rotate=2) == ERR_ARG
+    assert f(rotate=-1) == ERR_ARG
+    assert f(x=X + 8) == ERR_ALIGN
+    assert f(q=Q + 8) == ERR_ALIGN
+    assert f(s=S + 2) == ERR_ALIGN
+    assert f(g=G + 2) == ERR_ALIGN
+    assert f(a=A + 1) == ERR_ALIGN
+    # outputs overlapping the input or each other
+    assert f(q=X) == ERR_ARG
+    assert f(s=Q + 16) == ERR_ARG
+    assert f(g=S) == ERR_ARG
+    assert f(a=G) == ERR_ARG
+
+
+def test_empty_tensor_needs_only_the_scalars(lib):
+    # rows * cols == 0 with NULL tensors still validates the scalar pointers
+    assert rq(lib, x=None, q=None, s=None, rows=0, g=None) == ERR_NULL
+    assert rq(lib, x=None, q=None, s=None, rows=0, a=None) == ERR_NULL
+
+
+def test_rotamax_validation(lib):
+    f = lib.nvfp4_rotamax
+    assert f(None, 4, 64, 1, A, None) == ERR_NULL
+    assert f(X, 4, 64, 1, None, None) == ERR_NULL
+    assert f(X, 4, 40, 1, A, None) == ERR_SHAPE
+    assert f(X, 4, 64, 3, A, None) == ERR_ARG
+    assert f(X + 4, 4, 64, 1, A, None) == ERR_ALIGN
+    assert f(X, 4, 64, 1, A + 2, None) == ERR_ALIGN
+    assert f(X, 4, 64, 1, X + 64, None) == ERR_ARG
+
+
+def test_dequant_validation(lib):
+    f = lib.nvfp4_dequant
+    Y = 0x80000
+    assert f(None, S, G, 4, 64, 1, Y, None) == ERR_NULL
+    assert f(Q, None, G, 4, 64, 1, Y, None) == ERR_NULL
+    assert f(Q, S, None, 4, 64, 1, Y, None) == ERR_NULL
+    assert f(Q, S, G, 4, 64, 1, None, None) == ERR_NULL
+    assert f(Q, S, G, 4, 48 + 8, 1, Y, None) == ERR_SHAPE
+    assert f(Q, S, G, 4, 64, 7, Y, None) == ERR_ARG
+    assert f(Q + 4, S, G, 4, 64, 1, Y, None) == ERR_ALIGN
+    assert f(Q, S, G, 4, 64, 1, Y + 8, None) == ERR_ALIGN
+    assert f(Q, S, G, 4, 64, 1, Q, None) == ERR_ARG

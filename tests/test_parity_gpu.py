@@ -1,0 +1,276 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Bar: packed codes, block-scale bytes, the global scale and the amax are
+identical byte for byte (the method is a deterministic encoding: page "A Fused
+Hadamard + NVFP4 Quantization Kernel in Triton", sections 2-3).  The
+dequantized round-trip error agrees with the oracle's fp64 error within 1e-6
+relative.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def nv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_activation_amd as nv
+    return nv
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(x).to("cuda:0")
+
+
+def f32bits(v) -> int:
+    return int(np.asarray(v, dtype=np.float32).reshape(-1)[0].view(np.uint32))
+
+
+def compare(tag, x_np, rotate, got, ref=None):
+    """Byte-for-byte comparison with the oracle; a readable report on failure."""
+    q, s, g, a = [t.cpu().numpy() if torch.is_tensor(t) else t for t in got]
+    if ref is None:
+        ref = oracle.quantize(x_np, rotate)
+    oq, os_, og, oa = ref
+    msgs = []
+    if f32bits(a) != f32bits(oa):
+        msgs.append(f"amax {np.float32(a.reshape(-1)[0])!r} != oracle {oa!r}")
+    if f32bits(g) != f32bits(og):
+        msgs.append(f"gscale {np.float32(g.reshape(-1)[0])!r} != oracle {og!r}")
+    if not np.array_equal(s, os_):
+        bad = np.argwhere(s != os_)
+        msgs.append(f"{len(bad)} scale bytes differ, first {bad[0].tolist()}: "
+                    f"{s[tuple(bad[0])]:#04x} vs {os_[tuple(bad[0])]:#04x}")
+    if not np.array_equal(q, oq):
+        bad = np.argwhere(q != oq)
+        msgs.append(f"{len(bad)} code bytes differ, first {bad[0].tolist()}: "
+                    f"{q[tuple(bad[0])]:#04x} vs {oq[tuple(bad[0])]:#04x}")
+    assert not msgs, f"{tag}: " + "; ".join(msgs)
+
+
+# ---------------------------------------------------------------- small shapes
+
+SHAPES = [(1, 16), (3, 48), (127, 16), (5, 1024), (300, 4112), (1000, 1040), (257, 8192)]
+
+
+def mixed_input(rows, cols, dtype, seed):
+    """N(0,1) times a per-element log-normal spread of magnitudes, so sums in
+    the butterfly round and scales cover a wide range."""
+    n = rows * cols
+    z = synth.normal_f64(n, seed=seed, stream=1)
+    m = synth.normal_f64(n, seed=seed, stream=2)
+    v = z * np.exp(2.0 * m)
+    if dtype == "bf16":
+        return synth.round_bf16(v).reshape(rows, cols)
+    return v.astype(np.float32).reshape(rows, cols)
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_small_shapes(nv, rows, cols, dtype, rotate):
+    x = mixed_input(rows, cols, dtype, seed=rows * 7919 + cols)
+    got = nv.rotquant(to_dev(x), rotate=rotate)
+    torch.cuda.synchronize()
+    compare(f"{rows}x{cols} {dtype} rotate={rotate}", x, rotate, got)
+
+
+# ---------------------------------------------------------------- the workloads
+
+WORKLOAD_CASES = [(name, rot) for name, (_, _, _, rots) in synth.WORKLOADS.items() for rot in rots]
+
+
+@pytest.mark.parametrize("name,rotate", WORKLOAD_CASES)
+def test_workload_full_size(nv, name, rotate):
+    say(f"[parity] {name} rotate={rotate}: generating")
+    w = synth.make(name, rotate=rotate)
+    say(f"[parity] {name}: gpu")
+    xd = to_dev(w.x)
+    got = nv.rotquant(xd, rotate=rotate)
+    torch.cuda.synchronize()
+    got = [t.cpu() for t in got]
+    del xd
+    say(f"[parity] {name}: oracle")
+    ref = oracle.quantize(w.x, rotate)
+    compare(f"{name} rotate={rotate}", w.x, rotate, got, ref)
+    q, s, g, a = [t.numpy() for t in got]
+    # structural facts the recipes plant
+    assert s.max() == 0x7E
+    if name.startswith("silu_ties"):
+        assert g[0] == np.float32(1.0 / 16.0)
+        flags = w.meta["tie_flags"].astype(bool)
+        assert np.all(s.reshape(-1)[flags] == 0x58)      # E4M3 16.0
+    if name.startswith("kv_heads"):
+        kind = w.meta["block_kind"]
+        sb = s.reshape(-1)
+        assert np.all(sb[kind == 3] == 0x7E)
+        assert np.all(sb[(kind == 1) | (kind == 2)] == 0)
+        assert not q.reshape(-1, 8)[(kind == 1) | (kind == 2)].any()
+    say(f"[parity] {name}: ok")
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_all_zero_and_negative_zero(nv):
+    for dtype in ("bf16", "f32"):
+        x = np.zeros((7, 64), dtype=np.uint16 if dtype == "bf16" else np.float32)
+        if dtype == "bf16":
+            x[2] = 0x8000
+        else:
+            x[2] = -0.0
+        for rotate in (True, False):
+            got = nv.rotquant(to_dev(x), rotate=rotate)
+            torch.cuda.synchronize()
+            compare(f"zeros {dtype} rotate={rotate}", x, rotate, got)
+            assert got[2].item() == 1.0 and got[3].item() == 0.0
+
+
+def test_negative_zero_blocks_among_values(nv):
+    x = mixed_input(16, 256, "f32", seed=3)
+    x[3, 16:32] = -0.0
+    x[5, :] = -0.0
+    x[7, 48:64] = 0.0
+    for rotate in (True, False):
+        got = nv.rotquant(to_dev(x), rotate=rotate)
+        torch.cuda.synchronize()
+        compare(f"-0 blocks rotate={rotate}", x, rotate, got)
+
+
+def test_empty_tensors(nv):
+    for shape in ((0, 64), (5, 0), (0, 0)):
+        for dt in (torch.bfloat16, torch.float32):
+            x = torch.empty(shape, dtype=dt, device="cuda:0")
+            q, s, g, a = nv.rotquant(x, rotate=True)
+            torch.cuda.synchronize()
+            assert g.item() == 1.0 and a.item() == 0.0
+            assert q.numel() == 0 and s.numel() == 0
+
+
+def test_scale_rounds_to_zero_keeps_codes(nv):
+    """Divisor 1.0 path (section 2's guard for a zero scale): a block far below
+    the global amax gets scale 0 and codes of its raw values."""
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[0, 0] = 2.0 ** 20
+    x[1, :] = np.linspace(-6.0, 6.0, 64, dtype=np.float32)
+    got = nv.rotquant(to_dev(x), rotate=False)
+    torch.cuda.synchronize()
+    compare("zero scale", x, False, got)
+    ref = oracle.quantize(x, False)
+    assert ref[1][1].max() == 0 and ref[0][1].any()
+
+
+def test_e4m3_midpoint_scales(nv):
+    """Global amax 2688 makes g = 1 exactly; block maxima 6 * m put the block
+    value exactly on E4M3 midpoints m (ties to even)."""
+    vals = []
+    for e in range(-9, 9):
+        for k in range(16):
+            m = (8 + k + 0.5) * 2.0 ** (e - 3) if e >= -6 else (k + 0.5) * 2.0 ** -9
+            if 6 * m < 2688:
+                vals.append(6 * m)
+    n = len(vals) + 1
+    x = np.zeros((n, 16), dtype=np.float32)
+    x[0, 0] = 2688.0
+    for i, v in enumerate(vals):
+        x[i + 1, 3] = -v
+        x[i + 1, 7] = v / 3
+    for rotate in (False,):
+        got = nv.rotquant(to_dev(x), rotate=rotate)
+        torch.cuda.synchronize()
+        compare("e4m3 midpoints", x, rotate, got)
+
+
+def test_extreme_magnitudes(nv):
+    """Tiny (bf16 subnormal) and huge values; the contract allows |x| <= 2^123,
+    so that no butterfly sum of 16 values overflows."""
+    rng = np.random.default_rng(11)
+    for lo, hi in ((-133, -120), (-40, 40), (100, 121), (-133, 121)):
+        v = rng.standard_normal(64 * 128) * np.exp2(rng.integers(lo, hi, 64 * 128))
+        v[::17] = 0.0
+        for dtype in ("bf16", "f32"):
+            x = (synth.round_bf16(v) if dtype == "bf16" else v.astype(np.float32)).reshape(64, 128)
+            for rotate in (True, False):
+                got = nv.rotquant(to_dev(x), rotate=rotate)
+                torch.cuda.synchronize()
+                compare(f"magnitudes 2^{lo}..2^{hi} {dtype} rotate={rotate}", x, rotate, got)
+
+
+def test_quotients_near_e2m1_midpoints(nv):
+    """fp32, rotate off, g = 1 (amax 2688): blocks whose scale is 1.0 (max 6),
+    elements one ulp around each E2M1 midpoint and exactly on it."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+    cand = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 10)])
+    cand = np.concatenate([cand, -cand])
+    rows = (len(cand) + 14) // 15 + 1
+    x = np.zeros((rows, 16), dtype=np.float32)
+    x[0, 0] = 2688.0
+    flat = list(cand)
+    for r in range(1, rows):
+        x[r, 0] = 6.0
+        chunk = flat[(r - 1) * 15:(r - 1) * 15 + 15]
+        x[r, 1:1 + len(chunk)] = chunk
+    got = nv.rotquant(to_dev(x), rotate=False)
+    torch.cuda.synchronize()
+    compare("e2m1 midpoints", x, False, got)
+
+
+# ---------------------------------------------------------------- pass-level entry points
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_two_passes_equal_fused_call(nv, dtype):
+    x = mixed_input(512, 2048, dtype, seed=21)
+    xd = to_dev(x)
+    for rotate in (True, False):
+        amax = nv.rotamax(xd, rotate=rotate)
+        q, s, g = nv.quant_from_amax(xd, amax, rotate=rotate)
+        torch.cuda.synchronize()
+        compare(f"two passes {dtype} rotate={rotate}", x, rotate, (q, s, g, amax))
+
+
+def test_side_stream_and_repeat(nv):
+    x = mixed_input(1024, 4096, "bf16", seed=5)
+    xd = to_dev(x)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        r1 = nv.rotquant(xd, rotate=True)
+        r2 = nv.rotquant(xd, rotate=True)
+    st.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    compare("side stream", x, True, r1)
+
+
+# ---------------------------------------------------------------- round trip
+
+@pytest.mark.parametrize("name,rotate", WORKLOAD_CASES)
+def test_dequant_round_trip(nv, name, rotate):
+    w = synth.make(name, rotate=rotate, rows=min(synth.WORKLOADS[name][0], 2048))
+    xd = to_dev(w.x)
+    q, s, g, a = nv.rotquant(xd, rotate=rotate)
+    y = nv.dequant(q, s, g, rotate=rotate)
+    torch.cuda.synchronize()
+    xf = xd.double()
+    e_gpu = ((y.double() - xf).norm() / xf.norm()).item()
+    oq, os_, og, oa = oracle.quantize(w.x, rotate)
+    e_ora = oracle.roundtrip_error(w.x, rotate, oq, os_, og)
+    assert abs(e_gpu - e_ora) <= 1e-6 * e_ora, (e_gpu, e_ora)
+    # and element-wise against the oracle's fp64 decode
+    yd = oracle.dequant_f64(oq, os_, og, rotate)
+    scale = np.abs(yd).max()
+    assert np.max(np.abs(y.cpu().numpy().astype(np.float64) - yd)) <= 1e-6 * scale

@@ -23,189 +23,256 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cstdlib>
 #include <cstdint>
 #include <tuple>
 #include <utility>
 
 #include "nvfp4rq.h"
+#include "nvfp4rq_device.hpp"
 
 namespace {
 
-constexpr int kThreads = 256;        // 4 waves of 64
-constexpr int kMaxGrid = 8192;       // grid-stride beyond this
+using namespace nvfp4rq;
 
-// ---------------------------------------------------------------- loads
+constexpr int kThreads = 256;      // 4 waves of 64
+constexpr int kAmaxPieces = 8;     // 16-byte pieces per lane per iteration in the bf16 amax pass
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// One 16-value block as binary32 (bf16 widening is a shift: exact).
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t b, float v[16]) {
-  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
-  uint4 a = p[0];
-  uint4 c = p[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = bf16_lo(w[i]);
-    v[2 * i + 1] = bf16_hi(w[i]);
-  }
-}
-
-__device__ __forceinline__ void load_block(const float* __restrict__ x, int64_t b, float v[16]) {
-  const float4* p = reinterpret_cast<const float4*>(x + b * 16);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float4 t = p[i];
-    v[4 * i] = t.x;
-    v[4 * i + 1] = t.y;
-    v[4 * i + 2] = t.z;
-    v[4 * i + 3] = t.w;
-  }
-}
-
-// ---------------------------------------------------------------- rotation
-
-// z <- S16 z with S16 the unnormalised Sylvester matrix: butterfly stages with
-// strides 1, 2, 4, 8, each pair (a, b) -> (a + b, a - b).  H16 = S16 / 4
-// (section 1 and section 2, hadamard16).
-__device__ __forceinline__ void butterfly16(float z[16]) {
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((i & h) == 0) {
-        const float a = z[i];
-        const float b = z[i + h];
-        z[i] = a + b;
-        z[i + h] = a - b;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- scalar encodings
-
-// min(round-to-nearest-even onto E4M3, 448) for v >= 0, as the E4M3FN byte.
-// Normal range: round the binary32 mantissa to 3 bits (add half an E4M3 ulp
-// minus one, plus the lowest kept bit, then truncate); the carry moves into
-// the exponent by itself.  Below 2^-6 the quantum is 2^-9.
-__device__ __forceinline__ uint32_t e4m3_byte(float v) {
-  if (!(v < 448.0f)) return 0x7Eu;
-  if (v < 0x1p-6f) return static_cast<uint32_t>(__builtin_rintf(v * 512.0f));
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  return (u >> 20) - (120u << 3);   // rebias 127 -> 7 on the exponent field
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  if (b < 8u) return static_cast<float>(b) * 0x1p-9f;
-  return __uint_as_float((b + (120u << 3)) << 20);
-}
-
-// E2M1 code: midpoint compares, strict and non-strict alternating so that an
-// exact midpoint takes the even code; bit 3 when v < 0 (section 2, _e2m1_code).
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = __builtin_fabsf(v);
-  uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
-               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  return m + (v < 0.0f ? 8u : 0u);
-}
+// The fast path (corrected divisions with per-scale reciprocals) is used for
+// bf16 input when the global amax lies in [2^-38, 2^15): then every divisor is
+// in [2^-58.4, 2^14.4] and every quotient stays inside the range on which the
+// corrected division was enumerated.  Other tensors take the exact path
+// (IEEE divisions); both give identical bytes.
+constexpr uint32_t kFastAmaxLo = 0x2C800000u;   // 2^-38
+constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
 
 // ---------------------------------------------------------------- reductions
 
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), off, 64));
-    u = u > o ? u : o;
-  }
+  for (int off = 32; off >= 1; off >>= 1)
+    u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), off, 64)));
   return u;
 }
+
+// Workgroup maximum, then one atomicMax per workgroup.  Non-negative binary32
+// values order like their bit patterns, so the maximum is exact and the same
+// for any reduction order (a NaN input stays visible as bits above +inf).
+__device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restrict__ out) {
+  __shared__ uint32_t part[kThreads / 64];
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = part[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = umax(r, part[i]);
+    atomicMax(out, r);
+  }
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
 // ---------------------------------------------------------------- kernels
 
 __global__ void zero_word_kernel(uint32_t* __restrict__ w) { *w = 0u; }
 
-// Pass 1: rotated global amax (section 2: the global scale needs the amax of
-// the whole rotated tensor before any block is scaled).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void rotamax_kernel(const T* __restrict__ x, int64_t nb,
-                                                           int rotate,
-                                                           uint32_t* __restrict__ amax_bits) {
+// Pass 1 for bf16 (section 2: the global scale needs the amax of the whole
+// rotated tensor before any block can be scaled).  Coalesced: in each
+// iteration a wave reads 64 * kAmaxPieces consecutive 16-byte pieces, lane l
+// taking pieces l, l + 64, ...; a piece is half a block, so lanes 2k and 2k+1
+// hold elements 0..7 and 8..15 of one block.  Each lane runs the stride-1, 2,
+// 4 stages on its half; the stride-8 stage pairs the two lanes, and
+// max(|a + b|, |a - b|) = RN(|a| + |b|) exactly (rounding to nearest is
+// symmetric), so one DPP-fed add per element gives the block's largest |z|.
+// Both lanes compute the same sums; the maximum absorbs the duplicate.
+// max |0.25 z| = RN(0.25 max |z|) because rounding is monotone, so the scaling
+// is applied once at the end.
+template <bool ROTATE>
+__global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                int64_t nb,
+                                                                uint32_t* __restrict__ amax_bits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  const int64_t npieces = 2 * nb;
+  constexpr int64_t kPerWave = 64 * kAmaxPieces;
+  const uint4* __restrict__ p = reinterpret_cast<const uint4*>(x);
+  uint32_t m = 0u;
+  for (int64_t base = wave * kPerWave; base < npieces; base += nwaves * kPerWave) {
+    uint4 v[kAmaxPieces];
+    if (base + kPerWave <= npieces) {      // wave-uniform: every piece in range
+#pragma unroll
+      for (int j = 0; j < kAmaxPieces; ++j) v[j] = p[base + j * 64 + lane];
+    } else {                               // the tensor's last, partial chunk
+#pragma unroll
+      for (int j = 0; j < kAmaxPieces; ++j) {
+        const int64_t pc = base + j * 64 + lane;
+        v[j] = pc < npieces ? p[pc] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kAmaxPieces; ++j) {
+      float z[8];
+      widen8(v[j], z);
+      if (ROTATE) {
+        stages_1_2_4(z);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          m = umax(m, __float_as_uint(__builtin_fabsf(z[i]) + __builtin_fabsf(swap_lane1(z[i]))));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = umax(m, abs_bits(z[i]));
+      }
+    }
+  }
+  if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
+  workgroup_max_to(m, amax_bits);
+}
+
+// One 16-value fp32 block: elements 0..7 into lo, 8..15 into hi.
+__device__ __forceinline__ void load_block(const float* __restrict__ x, int64_t b, float lo[8],
+                                           float hi[8]) {
+  const float4* p = reinterpret_cast<const float4*>(x + b * 16);
+  const float4 a = p[0], c = p[1], d = p[2], e = p[3];
+  lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
+  lo[4] = c.x; lo[5] = c.y; lo[6] = c.z; lo[7] = c.w;
+  hi[0] = d.x; hi[1] = d.y; hi[2] = d.z; hi[3] = d.w;
+  hi[4] = e.x; hi[5] = e.y; hi[6] = e.z; hi[7] = e.w;
+}
+
+// One 16-value bf16 block (32 bytes), widened.
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t b, float lo[8],
+                                           float hi[8]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
+  widen8(p[0], lo);
+  widen8(p[1], hi);
+}
+
+// Pass 1 for fp32: one block per lane per iteration.
+template <bool ROTATE>
+__global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __restrict__ x,
+                                                               int64_t nb,
+                                                               uint32_t* __restrict__ amax_bits) {
   uint32_t m = 0u;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb;
-       b += stride) {
-    float v[16];
-    load_block(x, b, v);
-    if (rotate) butterfly16(v);
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb; b += stride) {
+    float lo[8], hi[8];
+    load_block(x, b, lo, hi);
+    if (ROTATE) {
+      stages_1_2_4(lo);
+      stages_1_2_4(hi);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;
-      m = m > a ? m : a;
+      for (int i = 0; i < 8; ++i)
+        m = umax(m, __float_as_uint(__builtin_fabsf(lo[i]) + __builtin_fabsf(hi[i])));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = umax(umax(m, abs_bits(lo[i])), abs_bits(hi[i]));
     }
   }
-  // max |0.25 z| = 0.25 max |z| exactly: rounding to nearest is monotone and
-  // the scaling by 0.25 commutes with it.
-  if (rotate) m = __float_as_uint(0.25f * __uint_as_float(m));
-  m = wave_max_u32(m);
-  __shared__ uint32_t part[kThreads / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) part[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = part[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) r = r > part[i] ? r : part[i];
-    atomicMax(amax_bits, r);
-  }
+  if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
+  workgroup_max_to(m, amax_bits);
 }
 
-// Global scale from the amax: (A / 6) / 448 in binary32, 1.0 when zero
-// (section 1 table; section 2, quantize).
-__device__ __forceinline__ float global_scale(float amax) {
-  float g = (amax / 6.0f) / 448.0f;
-  return g == 0.0f ? 1.0f : g;
-}
-
-// Pass 2: rotate + quantize, one block per lane per iteration (section 2,
-// hadamard_nvfp4_kernel).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
-                                                            int rotate,
-                                                            const uint32_t* __restrict__ amax_bits,
-                                                            uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s,
-                                                            float* __restrict__ gscale_out) {
-  const float g = global_scale(__uint_as_float(*amax_bits));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb;
-       b += stride) {
-    float y[16];
-    load_block(x, b, y);
-    if (rotate) {
-      butterfly16(y);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = 0.25f * y[i];
+// Pass 2 body: each lane rotates, scales and encodes one block per iteration.
+// Workgroup w handles the 256-block chunks w, w + G, w + 2G, ... (G = grid
+// size), last chunk first: the chunks pass 1 read last are the likeliest to
+// still be in the last-level cache.  Every step is the definition of section 2
+// (hadamard_nvfp4_kernel) in binary32:
+//   z     = S16 x                         (butterfly, no scaling yet)
+//   a_b   = max |y| = 0.25 max |z|        (exact for any rounding, see pass 1)
+//   v     = (a_b / 6) / g,  s = E4M3(min(v, 448))
+//   d     = float(s) * g, or 1 when that is 0
+//   code  = E2M1(y / d),  y = 0.25 z
+// FAST (bf16 in the guarded range): y / d = z / (4d) exactly (the scalings by
+// 4 are exact there), the divisions are corrected reciprocal products and the
+// per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
+// Otherwise every division is a true binary32 division.
+template <typename T, bool ROTATE, bool FAST>
+__device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
+                                             const float2* __restrict__ tab,
+                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t nchunks = (nb + kThreads - 1) / kThreads;
+  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const float rg = FAST ? 1.0f / g : 0.0f;
+  for (int64_t it = mine - 1; it >= 0; --it) {
+    const int64_t b = (it * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+    if (b >= nb) continue;
+    float lo[8], hi[8];
+    load_block(x, b, lo, hi);
+    if (ROTATE) {
+      stages_1_2_4(lo);
+      stages_1_2_4(hi);
+      stage_8(lo, hi);
     }
-    float ab = 0.0f;
+    float az = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ab = __builtin_fmaxf(ab, __builtin_fabsf(y[i]));
-    const float v = (ab / 6.0f) / g;
-    const uint32_t sb = e4m3_byte(v);
-    const float sf = e4m3_value(sb) * g;
-    const float d = (sf == 0.0f) ? 1.0f : sf;
-    uint32_t w[2] = {0u, 0u};
+    for (int i = 0; i < 8; ++i)
+      az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
+    uint32_t sb;
+    if (FAST) {
+      const float ab = ROTATE ? 0.25f * az : az;
+      const float a6 = div_corrected(ab, 6.0f, kRecip6);
+      sb = e4m3_byte(div_corrected(a6, g, rg));
+      const float2 t = tab[sb];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_code(y[i] / d) << (4 * (i & 7));
-    *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(w[0], w[1]);
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = div_corrected(lo[i], t.x, t.y);
+        hi[i] = div_corrected(hi[i], t.x, t.y);
+      }
+    } else {
+      if (ROTATE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo[i] = 0.25f * lo[i];
+          hi[i] = 0.25f * hi[i];
+        }
+      }
+      const float ab = ROTATE ? 0.25f * az : az;
+      sb = e4m3_byte((ab / 6.0f) / g);
+      const float sf = e4m3_value(sb) * g;
+      const float d = sf == 0.0f ? 1.0f : sf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = lo[i] / d + 0.0f;
+        hi[i] = hi[i] / d + 0.0f;
+      }
+    }
+    *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
     s[b] = static_cast<uint8_t>(sb);
   }
 }
 
-// Dequantize (section 2, dequantize): +-GRID[c & 7] * fl(float(s) * g), then
+template <typename T, bool ROTATE>
+__global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
+                                                            const uint32_t* __restrict__ amax_bits,
+                                                            int allow_fast,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ s,
+                                                            float* __restrict__ gscale_out) {
+  __shared__ float2 tab[128];
+  const uint32_t abits = *amax_bits;
+  const float g = global_scale(__uint_as_float(abits));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
+  if constexpr (sizeof(T) == 2) {
+    // uniform across the grid: every workgroup reads the same amax
+    if (allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
+      if (threadIdx.x < 128) {
+        const float sf = e4m3_value(threadIdx.x) * g;
+        const float d = (ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf);
+        tab[threadIdx.x] = make_float2(d, 1.0f / d);
+      }
+      __syncthreads();
+      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s);
+      return;
+    }
+  }
+  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s);
+}
+
+// Dequantize (section 2, dequantize): +-GRID[c & 7] * RN(float(s) * g), then
 // the same butterfly and * 0.25 when rotated (H16 is symmetric, so H16^T is
 // the forward transform).
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ q,
@@ -213,28 +280,33 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
                                                            const float* __restrict__ gscale,
                                                            int64_t nb, int rotate,
                                                            float* __restrict__ y) {
-  constexpr float kGrid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
   const float g = *gscale;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb;
        b += stride) {
     const uint2 w = *reinterpret_cast<const uint2*>(q + b * 8);
     const float sf = e4m3_value(s[b]) * g;
-    float v[16];
+    float lo[8], hi[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t c = ((i < 8 ? w.x : w.y) >> (4 * (i & 7))) & 15u;
-      const float mag = kGrid[c & 7u];
-      v[i] = ((c & 8u) ? -mag : mag) * sf;
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = e2m1_value((w.x >> (4 * i)) & 15u) * sf;
+      hi[i] = e2m1_value((w.y >> (4 * i)) & 15u) * sf;
     }
     if (rotate) {
-      butterfly16(v);
+      stages_1_2_4(lo);
+      stages_1_2_4(hi);
+      stage_8(lo, hi);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = 0.25f * lo[i];
+        hi[i] = 0.25f * hi[i];
+      }
     }
     float4* o = reinterpret_cast<float4*>(y + b * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    o[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
+    o[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
+    o[2] = make_float4(hi[0], hi[1], hi[2], hi[3]);
+    o[3] = make_float4(hi[4], hi[5], hi[6], hi[7]);
   }
 }
 
@@ -255,12 +327,54 @@ hipError_t launch(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t st, Ar
   return launch_impl(k, grid, block, st, std::index_sequence_for<KArgs...>{}, args...);
 }
 
-int grid_for(int64_t nb) {
-  int64_t g = (nb + kThreads - 1) / kThreads;
+// Compute units of the current device, cached per device.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    __atomic_store_n(&cache[dev], c, __ATOMIC_RELAXED);
+  }
+  return c;
+}
+
+// Positive integer from the environment, or 0.  Used to override launch
+// shapes in tests (results never depend on them).
+int64_t env_int(const char* name) {
+  const char* v = getenv(name);
+  if (!v || !*v) return 0;
+  char* end = nullptr;
+  const long long n = strtoll(v, &end, 10);
+  return (end && *end == '\0' && n > 0) ? n : 0;
+}
+
+int clamp_grid(int64_t want, int64_t needed) {
+  int64_t g = want < needed ? want : needed;
   if (g < 1) g = 1;
-  if (g > kMaxGrid) g = kMaxGrid;
+  if (g > (1 << 30)) g = 1 << 30;
   return static_cast<int>(g);
 }
+
+// Pass 1: 4 workgroups per compute unit, each wave streaming 8 KiB (bf16) per
+// iteration; fp32: one block per lane per iteration.
+int amax_grid(int64_t nb, bool bf16) {
+  int64_t want = env_int("NVFP4RQ_AMAX_WGS");
+  if (!want) want = 4LL * device_cus();
+  const int64_t per_wg = bf16 ? (kThreads / 64) * 64LL * kAmaxPieces / 2 : kThreads;  // blocks
+  return clamp_grid(want, (nb + per_wg - 1) / per_wg);
+}
+
+// Pass 2: 8 workgroups per compute unit, one 256-block chunk per iteration.
+int quant_grid(int64_t nb) {
+  int64_t want = env_int("NVFP4RQ_QUANT_WGS");
+  if (!want) want = 8LL * device_cus();
+  return clamp_grid(want, (nb + kThreads - 1) / kThreads);
+}
+
+int generic_grid(int64_t nb) { return clamp_grid(8LL * device_cus(), (nb + kThreads - 1) / kThreads); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -307,24 +421,42 @@ nvfp4_status validate_quant(const T* x, int64_t rows, int64_t cols, int rotate, 
 }
 
 template <typename T>
+hipError_t launch_rotamax(const T* x, int64_t nb, int rotate, uint32_t* bits, hipStream_t st);
+
+template <>
+hipError_t launch_rotamax<uint16_t>(const uint16_t* x, int64_t nb, int rotate, uint32_t* bits,
+                                    hipStream_t st) {
+  const dim3 grid(amax_grid(nb, true));
+  return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits)
+                : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits);
+}
+
+template <>
+hipError_t launch_rotamax<float>(const float* x, int64_t nb, int rotate, uint32_t* bits,
+                                 hipStream_t st) {
+  const dim3 grid(amax_grid(nb, false));
+  return rotate ? launch(rotamax_f32_kernel<true>, grid, dim3(kThreads), st, x, nb, bits)
+                : launch(rotamax_f32_kernel<false>, grid, dim3(kThreads), st, x, nb, bits);
+}
+
+template <typename T>
 nvfp4_status enqueue_rotamax(const T* x, int64_t nb, int rotate, float* amax, hipStream_t st) {
   uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
   if (launch(zero_word_kernel, dim3(1), dim3(1), st, bits) != hipSuccess) return NVFP4_ERR_HIP;
   if (nb == 0) return NVFP4_OK;
-  if (launch(rotamax_kernel<T>, dim3(grid_for(nb)), dim3(kThreads), st, x, nb, rotate, bits) !=
-      hipSuccess)
-    return NVFP4_ERR_HIP;
-  return NVFP4_OK;
+  return launch_rotamax(x, nb, rotate, bits, st) == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 template <typename T>
 nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const float* amax, uint8_t* q,
                            uint8_t* s, float* g, hipStream_t st) {
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(amax);
-  if (launch(rotquant_kernel<T>, dim3(grid_for(nb)), dim3(kThreads), st, x, nb, rotate, bits, q,
-             s, g) != hipSuccess)
-    return NVFP4_ERR_HIP;
-  return NVFP4_OK;
+  const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
+  const dim3 grid(quant_grid(nb));
+  const hipError_t e =
+      rotate ? launch(rotquant_kernel<T, true>, grid, dim3(kThreads), st, x, nb, bits, allow_fast, q, s, g)
+             : launch(rotquant_kernel<T, false>, grid, dim3(kThreads), st, x, nb, bits, allow_fast, q, s, g);
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 template <typename T>
@@ -418,7 +550,7 @@ nvfp4_status nvfp4_dequant(const uint8_t* q, const uint8_t* s, const float* gsca
       overlap(ry, range_of(gscale, 4)))
     return NVFP4_ERR_ARG;
   if (nb == 0) return NVFP4_OK;
-  if (launch(dequant_kernel, dim3(grid_for(nb)), dim3(kThreads), stream, q, s, gscale, nb, rotate,
+  if (launch(dequant_kernel, dim3(generic_grid(nb)), dim3(kThreads), stream, q, s, gscale, nb, rotate,
              y_out) != hipSuccess)
     return NVFP4_ERR_HIP;
   return NVFP4_OK;

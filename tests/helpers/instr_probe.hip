@@ -1,0 +1,60 @@
+// GPU side of the instruction checks (test code): runs the library's own
+// conversion helpers (nvfp4rq_device.hpp) over ranges of binary32 bit
+// patterns so that the tests can compare every output with the CPU oracle.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "nvfp4rq_device.hpp"
+
+using namespace nvfp4rq;
+
+// one byte per input: the E2M1 code e2m1_pack8 gives to value base + i
+__global__ void e2m1_kernel(uint32_t base, uint32_t n, uint8_t* __restrict__ out) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = __uint_as_float(base + i);
+  float q[8] = {v, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  out[i] = static_cast<uint8_t>(e2m1_pack8(q) & 15u);
+}
+
+// one byte per input: e4m3_byte(base + i)
+__global__ void e4m3_kernel(uint32_t base, uint32_t n, uint8_t* __restrict__ out) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = static_cast<uint8_t>(e4m3_byte(__uint_as_float(base + i)));
+}
+
+// 16 values -> 8 packed bytes, to check the nibble order
+__global__ void pack_kernel(const float* __restrict__ v, uint32_t* __restrict__ out) {
+  float a[8], b[8];
+  for (int i = 0; i < 8; ++i) { a[i] = v[i]; b[i] = v[8 + i]; }
+  out[0] = e2m1_pack8(a);
+  out[1] = e2m1_pack8(b);
+}
+
+// all 256 E4M3 byte values -> float (e4m3_value) and all 16 codes -> e2m1_value
+__global__ void values_kernel(float* __restrict__ e4m3, float* __restrict__ e2m1) {
+  const uint32_t i = threadIdx.x;
+  e4m3[i] = e4m3_value(i);
+  if (i < 16) e2m1[i] = e2m1_value(i);
+}
+
+extern "C" {
+int probe_e2m1(uint32_t base, uint32_t n, uint8_t* out, hipStream_t st) {
+  e2m1_kernel<<<(n + 255) / 256, 256, 0, st>>>(base, n, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+int probe_e4m3(uint32_t base, uint32_t n, uint8_t* out, hipStream_t st) {
+  e4m3_kernel<<<(n + 255) / 256, 256, 0, st>>>(base, n, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+int probe_pack(const float* v, uint32_t* out, hipStream_t st) {
+  pack_kernel<<<1, 1, 0, st>>>(v, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+int probe_values(float* e4m3, float* e2m1, hipStream_t st) {
+  values_kernel<<<1, 256, 0, st>>>(e4m3, e2m1);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+}

@@ -167,7 +167,8 @@ def test_scale_rounds_to_zero_keeps_codes(nv):
     the global amax gets scale 0 and codes of its raw values."""
     x = np.zeros((2, 64), dtype=np.float32)
     x[0, 0] = 2.0 ** 20
-    x[1, :] = np.linspace(-6.0, 6.0, 64, dtype=np.float32)
+    # (2 / 6) / g = 2 * 2688 / (6 * 2^20) < 2^-10, so the block scale rounds to 0
+    x[1, :] = np.linspace(-2.0, 2.0, 64, dtype=np.float32)
     got = nv.rotquant(to_dev(x), rotate=False)
     torch.cuda.synchronize()
     compare("zero scale", x, False, got)
@@ -228,6 +229,59 @@ def test_quotients_near_e2m1_midpoints(nv):
     got = nv.rotquant(to_dev(x), rotate=False)
     torch.cuda.synchronize()
     compare("e2m1 midpoints", x, False, got)
+
+
+# ---------------------------------------------------------------- paths and launch shapes
+
+EXACT_CASES = [("gauss_outliers_128x1024", True), ("gauss_1pct_cols_4096x4096", False),
+               ("silu_ties_32768x14336", True), ("silu_ties_32768x14336", False),
+               ("t3_lognormal_16384x8192", True)]
+
+
+@pytest.mark.parametrize("name,rotate", EXACT_CASES)
+def test_exact_path_equals_oracle(nv, monkeypatch, name, rotate):
+    """The all-IEEE-division path (taken outside the fast range, and forced
+    here) gives the same bytes as the oracle and as the fast path."""
+    w = synth.make(name, rotate=rotate, rows=min(synth.WORKLOADS[name][0], 512))
+    xd = to_dev(w.x)
+    fast = nv.rotquant(xd, rotate=rotate)
+    monkeypatch.setenv("NVFP4RQ_EXACT_ONLY", "1")
+    exact = nv.rotquant(xd, rotate=rotate)
+    torch.cuda.synchronize()
+    compare(f"{name} exact path", w.x, rotate, exact)
+    for a, b in zip(fast, exact):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_launch_shape_invariance(nv, monkeypatch, dtype):
+    """Outputs do not depend on the number of workgroups (the page's first
+    "Try this": results must not depend on tiling)."""
+    x = mixed_input(777, 2064, dtype, seed=99)
+    xd = to_dev(x)
+    ref = [t.clone() for t in nv.rotquant(xd, rotate=True)]
+    torch.cuda.synchronize()
+    compare(f"default shape {dtype}", x, True, ref)
+    for a_wgs, q_wgs in ((1, 1), (3, 7), (64, 5), (1000, 4096), (2, 100000)):
+        monkeypatch.setenv("NVFP4RQ_AMAX_WGS", str(a_wgs))
+        monkeypatch.setenv("NVFP4RQ_QUANT_WGS", str(q_wgs))
+        got = nv.rotquant(xd, rotate=True)
+        torch.cuda.synchronize()
+        for r, g in zip(ref, got):
+            assert torch.equal(r, g), (a_wgs, q_wgs)
+
+
+@pytest.mark.parametrize("target", [2.0 ** 15 * 0.999, 2.0 ** 15, 2.0 ** 15 * 1.01,
+                                    2.0 ** -38, 2.0 ** -38 * 0.99, 2.0 ** -38 * 1.01])
+def test_fast_range_edges(nv, target):
+    """Tensors whose amax sits at either edge of the fast path's range."""
+    base = mixed_input(64, 512, "f32", seed=7).astype(np.float64)
+    for rotate in (True, False):
+        v = base / np.abs(base).max() * target
+        x = synth.round_bf16(v).reshape(64, 512)
+        got = nv.rotquant(to_dev(x), rotate=rotate)
+        torch.cuda.synchronize()
+        compare(f"amax ~ {target!r} rotate={rotate}", x, rotate, got)
 
 
 # ---------------------------------------------------------------- pass-level entry points

@@ -257,6 +257,9 @@ def main() -> int:
         "pass1_ms": round(statistics.mean(p1_ms), 5),
         "pass2_ms": round(p2, 5),
         "pass1_gbs": round(nbytes["pass1"] / (statistics.mean(p1_ms) * 1e-3) / 1e9, 2),
+        # pass 2 alone is the single-pass quantizer with a given amax
+        # (2.5625 B per element)
+        "given_scale_single_pass_gbs": round(p2_gbs, 2),
         "roofline": {"bound": "hbm", "kernel": "rotquant (pass 2)",
                      "achieved": round(p2_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(p2_gbs / HBM_PEAK_GBS, 4),

@@ -111,9 +111,14 @@ nvfp4_status nvfp4_rotamax_f32(const float *x, int64_t rows, int64_t cols, int r
                                float *amax_out, hipStream_t stream);
 
 /*
- * Pass 2 alone: reads the amax from device memory (as written by
- * nvfp4_rotamax), derives the global scale, writes it to *gscale_out and
- * quantizes every block.  Section 2 of the same page (hadamard_nvfp4_kernel).
+ * Pass 2 alone: reads an amax from device memory, derives the global scale
+ * (amax / 6) / 448, writes it to *gscale_out and quantizes every block.
+ * Section 2 of the same page (hadamard_nvfp4_kernel).  With the amax written
+ * by nvfp4_rotamax on the same tensor this completes nvfp4_rotquant; with an
+ * amax kept from an earlier step it is the single-pass quantizer the page's
+ * section 2 notes for production use (one read of x instead of two).  Then
+ * block values above 448 are clamped to 448 and quotients beyond 6 take the
+ * largest code, exactly as the definition gives.
  *   amax_in  device, 1 float, 4-byte aligned, finite and >= 0.
  * Other arguments as nvfp4_rotquant.
  */

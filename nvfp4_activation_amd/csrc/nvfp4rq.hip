@@ -45,6 +45,10 @@ constexpr int kAmaxPieces = 8;     // 16-byte pieces per lane per iteration in t
 // (IEEE divisions); both give identical bytes.
 constexpr uint32_t kFastAmaxLo = 0x2C800000u;   // 2^-38
 constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
+// Corrected divisions stay finite while |z| / d <= 2^100; larger quotients
+// (possible only when the global scale comes from another tensor's amax) take
+// true divisions.
+constexpr float kQuotientLimit = 0x1p100f;
 
 // ---------------------------------------------------------------- reductions
 
@@ -215,12 +219,26 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
     if (FAST) {
       const float ab = ROTATE ? 0.25f * az : az;
       const float a6 = div_corrected(ab, 6.0f, kRecip6);
+      // A quotient too large for binary32 makes the product NaN; fminf keeps
+      // 448, the right byte for any block value that large.
       sb = e4m3_byte(div_corrected(a6, g, rg));
       const float2 t = tab[sb];
+      if (az <= kQuotientLimit * t.x) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo[i] = div_corrected(lo[i], t.x, t.y);
-        hi[i] = div_corrected(hi[i], t.x, t.y);
+        for (int i = 0; i < 8; ++i) {
+          lo[i] = div_corrected(lo[i], t.x, t.y);
+          hi[i] = div_corrected(hi[i], t.x, t.y);
+        }
+      } else {
+        // Only with a global scale from elsewhere (the amax of an earlier
+        // step) can a block's quotients approach the binary32 range; divide
+        // exactly (y = z / 4 and d = 4d / 4 are exact here).
+        const float d = ROTATE ? 0.25f * t.x : t.x;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
+          hi[i] = (ROTATE ? 0.25f * hi[i] : hi[i]) / d + 0.0f;
+        }
       }
     } else {
       if (ROTATE) {

@@ -61,6 +61,15 @@ def rn32(x: F) -> F:
     return -r if neg else r
 
 
+def rn32_sat(x: F) -> F:
+    """rn32, with results beyond the largest binary32 given as +-2^128 (they
+    stand for +-inf: every such quotient has the largest E2M1 code)."""
+    try:
+        return rn32(x)
+    except OverflowError:
+        return F(2) ** 128 if x > 0 else -(F(2) ** 128)
+
+
 # ------------------------------------------------------------------ grids
 
 GRID_E2M1 = [F(0), F(1, 2), F(1), F(3, 2), F(2), F(3), F(4), F(6)]
@@ -117,34 +126,51 @@ def rotate16(x: list[F]) -> list[F]:
     return [rn32(F(1, 4) * v) for v in z]
 
 
+def _blocks(x_f32: np.ndarray, rotate: bool):
+    flat = x_f32.reshape(-1)
+    out = []
+    for b in range(flat.size // 16):
+        xb = [f32_to_frac(v) for v in flat[16 * b:16 * b + 16]]
+        out.append(rotate16(xb) if rotate else xb)
+    return out
+
+
+def global_scale(amax: F) -> F:
+    g = rn32(rn32(amax / 6) / 448)
+    return F(1) if g == 0 else g
+
+
 def quantize(x_f32: np.ndarray, rotate: bool):
     """x_f32: float32 [rows, cols] (bf16 inputs are widened exactly first).
     Returns (q uint8 [rows, cols/2], s uint8 [rows, cols/16], g float32, amax float32)."""
-    rows, cols = x_f32.shape
-    nb = rows * cols // 16
-    flat = x_f32.reshape(-1)
-    blocks = []
-    for b in range(nb):
-        xb = [f32_to_frac(v) for v in flat[16 * b:16 * b + 16]]
-        blocks.append(rotate16(xb) if rotate else xb)
+    blocks = _blocks(x_f32, rotate)
     amax = max((abs(v) for blk in blocks for v in blk), default=F0)
-    g = rn32(rn32(amax / 6) / 448)
-    if g == 0:
-        g = F(1)
+    g = global_scale(amax)
+    q, s = _encode(blocks, g, x_f32.shape)
+    return q, s, frac_to_f32(g), frac_to_f32(amax)
+
+
+def quantize_given_scale(x_f32: np.ndarray, rotate: bool, g: F):
+    """Same block arithmetic with a global scale supplied by the caller."""
+    return _encode(_blocks(x_f32, rotate), g, x_f32.shape)
+
+
+def _encode(blocks, g: F, shape):
+    rows, cols = shape
+    nb = rows * cols // 16
     q = np.zeros(nb * 8, dtype=np.uint8)
     s = np.zeros(nb, dtype=np.uint8)
     for b, y in enumerate(blocks):
         ab = max(abs(v) for v in y)
-        v = rn32(rn32(ab / 6) / g)
+        v = rn32_sat(rn32(ab / 6) / g)
         sb = e4m3_nearest(v)
         sf = rn32(E4M3_VALUES[sb] * g)
         d = F(1) if sf == 0 else sf
-        codes = [e2m1_nearest(rn32(yi / d)) for yi in y]
+        codes = [e2m1_nearest(rn32_sat(yi / d)) for yi in y]
         for k in range(8):
             q[8 * b + k] = codes[2 * k] | (codes[2 * k + 1] << 4)
         s[b] = sb
-    return (q.reshape(rows, cols // 2), s.reshape(rows, cols // 16), frac_to_f32(g),
-            frac_to_f32(amax))
+    return q.reshape(rows, cols // 2), s.reshape(rows, cols // 16)
 
 
 def f32_bits(x: np.float32) -> int:

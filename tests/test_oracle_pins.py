@@ -279,6 +279,44 @@ def test_oracle_matches_exact_rational_model():
     assert n == 1500
 
 
+def test_given_scale_matches_exact_model():
+    """Quantization with a caller-supplied global scale (an amax from an
+    earlier step, section 2's note on reusing an amax): the block value can
+    pass 448 and is clamped there; quotients can pass 6 and saturate."""
+    rng = np.random.default_rng(17)
+    n = 0
+    for x, xf, rotate in _tiny_inputs(300):
+        true_amax = float(np.abs(xf).max()) or 1.0
+        for factor in (1e-6, 0.01, 0.37, 1.0, 3.0):
+            amax_given = np.float32(true_amax * factor * rng.uniform(0.5, 2.0))
+            g = oracle.global_scale(amax_given)
+            q, s = oracle.quantize_given_scale(x, rotate, g)
+            mq, ms = em.quantize_given_scale(xf, rotate, em.f32_to_frac(g))
+            assert np.array_equal(q, mq) and np.array_equal(s, ms), (x, rotate, g)
+            n += 1
+    assert n == 1500
+
+
+def test_given_scale_with_own_amax_is_the_full_method():
+    for name in ("gauss_outliers_128x1024", "kv_heads_65536x8x128_f32"):
+        w = synth.make(name, rows=64)
+        for rotate in (True, False):
+            q, s, g, a = oracle.quantize(w.x, rotate)
+            q2, s2 = oracle.quantize_given_scale(w.x, rotate, oracle.global_scale(a))
+            assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_given_scale_saturates_blocks_at_448():
+    """A global scale 100x too small puts most block values above 448: the
+    scale byte is 0x7E and the largest codes saturate at 7."""
+    x = synth.normal_bf16(32 * 256, seed=9).reshape(32, 256)
+    q, s, g, a = oracle.quantize(x, True)
+    q2, s2 = oracle.quantize_given_scale(x, True, oracle.global_scale(a / 100))
+    assert (s2 == 0x7E).mean() > 0.9
+    codes = np.stack([q2 & 15, q2 >> 4], -1)
+    assert ((codes & 7) == 7).mean() > 0.2
+
+
 def test_divisor_one_when_scale_rounds_to_zero():
     """When a block's scale rounds to E4M3 zero the divisor is 1.0 and codes
     come from the raw values (section 2, the where(s_f == 0, 1, s_f) guard)."""

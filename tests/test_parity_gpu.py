@@ -284,6 +284,49 @@ def test_fast_range_edges(nv, target):
         compare(f"amax ~ {target!r} rotate={rotate}", x, rotate, got)
 
 
+# ---------------------------------------------------------------- given global scale
+
+GIVEN_CASES = [("gauss_outliers_128x1024", True), ("t3_lognormal_16384x8192", True),
+               ("silu_ties_32768x14336", False), ("kv_heads_65536x8x128_f32", True)]
+
+
+@pytest.mark.parametrize("name,rotate", GIVEN_CASES)
+def test_given_scale_single_pass(nv, name, rotate):
+    """Pass 2 with an amax from elsewhere (an earlier step): block values can
+    exceed 448 (clamped) and quotients 6 (largest code).  Against the oracle's
+    quantizer with the same global scale."""
+    w = synth.make(name, rotate=rotate, rows=min(synth.WORKLOADS[name][0], 1024))
+    xd = to_dev(w.x)
+    true_amax = oracle.amax(w.x, rotate)
+    for factor in (1e-6, 0.01, 0.3, 1.0, 2.0, 1e4):
+        amax = np.float32(true_amax * factor)
+        a = torch.tensor([amax], dtype=torch.float32, device="cuda:0")
+        q, s, g = nv.quant_from_amax(xd, a, rotate=rotate)
+        torch.cuda.synchronize()
+        og = oracle.global_scale(amax)
+        oq, os_ = oracle.quantize_given_scale(w.x, rotate, og)
+        compare(f"{name} given amax x{factor}", w.x, rotate, (q, s, g, a), (oq, os_, og, amax))
+
+
+def test_given_scale_huge_quotients(nv):
+    """Values up to 2^100 with a global scale from amax 1: quotients far
+    beyond binary32's reach of the corrected division take true divisions."""
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(64 * 256) * np.exp2(rng.integers(-20, 101, 64 * 256))
+    for dtype in ("bf16", "f32"):
+        x = (synth.round_bf16(v) if dtype == "bf16" else v.astype(np.float32)).reshape(64, 256)
+        xd = to_dev(x)
+        for rotate in (True, False):
+            for amax in (np.float32(1.0), np.float32(2.0 ** -30), np.float32(1000.0)):
+                a = torch.tensor([amax], dtype=torch.float32, device="cuda:0")
+                q, s, g = nv.quant_from_amax(xd, a, rotate=rotate)
+                torch.cuda.synchronize()
+                og = oracle.global_scale(amax)
+                oq, os_ = oracle.quantize_given_scale(x, rotate, og)
+                compare(f"huge {dtype} rotate={rotate} amax={amax}", x, rotate, (q, s, g, a),
+                        (oq, os_, og, amax))
+
+
 # ---------------------------------------------------------------- pass-level entry points
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

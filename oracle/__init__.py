@@ -62,6 +62,14 @@ def _load():
     lib.oracle_e2m1_code_array.argtypes = [_ptr, _i64, _ptr, _int]
     lib.oracle_e4m3_byte_array.argtypes = [_ptr, _i64, _ptr, _int]
     lib.oracle_e2m1_code_bits.argtypes = [_u32, _u32, _ptr, _int]
+    lib.oracle_e8m0_byte.argtypes = [_f32]
+    lib.oracle_e8m0_byte.restype = ctypes.c_uint8
+    lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_value.restype = _f32
+    lib.oracle_mx_quantize.argtypes = [_ptr, _int, _i64, _i64, _int, _ptr, _ptr, _int]
+    lib.oracle_mx_quantize.restype = _int
+    lib.oracle_mx_roundtrip_error.argtypes = [_ptr, _int, _i64, _i64, _int, _ptr, _ptr, _int]
+    lib.oracle_mx_roundtrip_error.restype = ctypes.c_double
     lib.oracle_e4m3_byte_bits.argtypes = [_u32, _u32, _ptr, _int]
     _lib = lib
     return lib
@@ -187,3 +195,36 @@ def roundtrip_error(x: np.ndarray, rotate: bool, q: np.ndarray, s: np.ndarray, g
         _p(x), _is_f32(x), rows, cols, int(rotate), _p(np.ascontiguousarray(q)),
         _p(np.ascontiguousarray(s)), float(np.float32(g)),
         None if cm is None else _p(cm), nthreads))
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+
+def e8m0_byte(t: float) -> int:
+    """Byte of the smallest power of two >= t (exponent clamped to [-127, 127])."""
+    return int(_load().oracle_e8m0_byte(float(np.float32(t))))
+
+
+def e8m0_value(b: int) -> float:
+    return float(_load().oracle_e8m0_value(int(b)))
+
+
+def mx_quantize(x: np.ndarray, rotate: bool, nthreads: int = 0):
+    """MXFP4: returns (q uint8 [rows, cols/2], s uint8 [rows, cols/32] E8M0 bytes)."""
+    rows, cols = x.shape
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty((rows, cols // 32), dtype=np.uint8)
+    rc = _load().oracle_mx_quantize(_p(x), _is_f32(x), rows, cols, int(rotate), _p(q), _p(s),
+                                    nthreads)
+    if rc:
+        raise ValueError("oracle_mx_quantize rejected its arguments")
+    return q, s
+
+
+def mx_roundtrip_error(x: np.ndarray, rotate: bool, q: np.ndarray, s: np.ndarray,
+                       nthreads: int = 0) -> float:
+    rows, cols = x.shape
+    return float(_load().oracle_mx_roundtrip_error(
+        _p(x), _is_f32(x), rows, cols, int(rotate), _p(np.ascontiguousarray(q)),
+        _p(np.ascontiguousarray(s)), nthreads))

@@ -462,3 +462,151 @@ void oracle_e4m3_byte_bits(uint32_t lo, uint32_t hi, uint8_t *out, int nthreads)
     }
     (void)nthreads;
 }
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 variant: 32-element blocks, power-of-two (E8M0) scales        */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The page "A Fused Hadamard + NVFP4 Quantization Kernel in Triton" contrasts
+ * NVFP4 with MXFP4 (section 1: 32-element blocks, power-of-two E8M0 scales;
+ * its "Try this" list asks for the error study under MXFP4 semantics).  The
+ * page "Hopper kernel for MXFP4" stores each MX scale as one unsigned byte
+ * holding a binary exponent (value 2^(byte - 127)).  Readings where the pages
+ * stop short:
+ *   - the rotation stays the 16-point block rotation, applied to each half of
+ *     a 32-element block;
+ *   - the block value is fl(amax / 6) as in the NVFP4 recipe, and the scale is
+ *     the smallest power of two at or above it, so the block's largest value
+ *     maps into (3, 6] (never clipped), exponent clamped to [-127, 127];
+ *     an all-zero block gets the byte 0;
+ *   - element values v = fl(y / scale) (an exact power-of-two scaling except
+ *     on underflow), then the same E2M1 midpoint rule and sign rule;
+ *   - storage: codes [rows, cols/2] as for NVFP4, scales [rows, cols/32].
+ */
+uint8_t oracle_e8m0_byte(float t)
+{
+    if (!(t > 0.0f))
+        return 0;
+    int fe;
+    float m = frexpf(t, &fe);      /* t = m * 2^fe, m in [0.5, 1) */
+    int e = (m == 0.5f) ? fe - 1 : fe;   /* ceil(log2 t) */
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return (uint8_t)(e + 127);
+}
+
+float oracle_e8m0_value(uint8_t b)
+{
+    return ldexpf(1.0f, (int)b - 127);
+}
+
+static void load_span(const void *x, int is_f32, int64_t start, int n, float *out)
+{
+    if (is_f32) {
+        const float *p = (const float *)x + start;
+        for (int i = 0; i < n; i++)
+            out[i] = p[i];
+    } else {
+        const uint16_t *p = (const uint16_t *)x + start;
+        for (int i = 0; i < n; i++)
+            out[i] = bf16_to_float(p[i]);
+    }
+}
+
+/* One 32-element MX block: optional rotation of each half, E8M0 scale, codes. */
+static void mx_block(const float *xb, int rotate, uint8_t *q16, uint8_t *s1)
+{
+    float y[32];
+    if (rotate) {
+        oracle_rotate16(xb, y);
+        oracle_rotate16(xb + 16, y + 16);
+    } else {
+        for (int i = 0; i < 32; i++)
+            y[i] = xb[i];
+    }
+    float ab = 0.0f;
+    for (int i = 0; i < 32; i++) {
+        float a = fabsf(y[i]);
+        if (a > ab)
+            ab = a;
+    }
+    uint8_t s = oracle_e8m0_byte(ab / 6.0f);
+    float scale = oracle_e8m0_value(s);
+    uint8_t code[32];
+    for (int i = 0; i < 32; i++)
+        code[i] = oracle_e2m1_code(y[i] / scale);
+    for (int k = 0; k < 16; k++)
+        q16[k] = (uint8_t)(code[2 * k] | (code[2 * k + 1] << 4));
+    *s1 = s;
+}
+
+/* MXFP4 quantization of a [rows, cols] tensor, cols % 32 == 0.  Returns 0, or
+   -1 on a bad shape. */
+int oracle_mx_quantize(const void *x, int is_f32, int64_t rows, int64_t cols, int rotate,
+                       uint8_t *q, uint8_t *s, int nthreads)
+{
+    if (cols % 32 != 0 || rows < 0 || cols < 0)
+        return -1;
+    int64_t nb = rows * (cols / 32);
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+#endif
+    for (int64_t b = 0; b < nb; b++) {
+        float xb[32];
+        load_span(x, is_f32, b * 32, 32, xb);
+        mx_block(xb, rotate, q + 16 * b, s + b);
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* Relative L2 round-trip error of an MXFP4 encoding (fp64 sums, exact H). */
+double oracle_mx_roundtrip_error(const void *x, int is_f32, int64_t rows, int64_t cols,
+                                 int rotate, const uint8_t *q, const uint8_t *s, int nthreads)
+{
+    int64_t nb = rows * (cols / 32);
+    double num = 0.0, den = 0.0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) reduction(+ : num, den) schedule(static)
+#endif
+    for (int64_t b = 0; b < nb; b++) {
+        float xb[32];
+        load_span(x, is_f32, b * 32, 32, xb);
+        float scale = oracle_e8m0_value(s[b]);
+        double yh[32], xh[32];
+        for (int i = 0; i < 32; i++) {
+            int c = (i & 1) ? (q[16 * b + i / 2] >> 4) : (q[16 * b + i / 2] & 15);
+            float mag = (float)E2M1_GRID[c & 7];
+            float val = (c & 8) ? -mag : mag;
+            yh[i] = (double)(val * scale);
+        }
+        for (int h = 0; h < 2; h++) {
+            for (int i = 0; i < 16; i++) {
+                if (!rotate) {
+                    xh[16 * h + i] = yh[16 * h + i];
+                    continue;
+                }
+                double acc = 0.0;
+                for (int j = 0; j < 16; j++) {
+                    int sign = __builtin_popcount((unsigned)(i & j)) & 1;
+                    acc += (sign ? -yh[16 * h + j] : yh[16 * h + j]) * 0.25;
+                }
+                xh[16 * h + i] = acc;
+            }
+        }
+        for (int i = 0; i < 32; i++) {
+            double d = xh[i] - (double)xb[i];
+            num += d * d;
+            den += (double)xb[i] * (double)xb[i];
+        }
+    }
+    (void)nthreads;
+    return sqrt(num) / sqrt(den);
+}

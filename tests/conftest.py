@@ -48,7 +48,7 @@ def sweeps_lib(tmp_path_factory):
                     os.path.join(TESTS, "helpers", "sweeps.c"), "-o", str(out),
                     f"-L{odir}", "-lnvfp4oracle", f"-Wl,-rpath,{odir}", "-lm"], check=True)
     lib = ctypes.CDLL(str(out))
-    for name in ("sweep_e2m1_all",):
+    for name in ("sweep_e2m1_all", "sweep_e8m0_all"):
         getattr(lib, name).restype = ctypes.c_longlong
         getattr(lib, name).argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.sweep_e4m3_range.restype = ctypes.c_longlong

@@ -175,3 +175,35 @@ def _encode(blocks, g: F, shape):
 
 def f32_bits(x: np.float32) -> int:
     return struct.unpack("<I", struct.pack("<f", float(x)))[0]
+
+
+# ------------------------------------------------------------------ MXFP4 variant
+
+def e8m0_smallest_power_at_or_above(t: F) -> int:
+    """Byte of the smallest power of two >= t, exponent clamped to [-127, 127];
+    0 for t == 0 (search over the 255 representable scales)."""
+    if t == 0:
+        return 0
+    for b in range(255):
+        if F(2) ** (b - 127) >= t:
+            return b
+    return 254
+
+
+def mx_quantize(x_f32: np.ndarray, rotate: bool):
+    rows, cols = x_f32.shape
+    flat = x_f32.reshape(-1)
+    nb = flat.size // 32
+    q = np.zeros(nb * 16, dtype=np.uint8)
+    s = np.zeros(nb, dtype=np.uint8)
+    for b in range(nb):
+        xb = [f32_to_frac(v) for v in flat[32 * b:32 * b + 32]]
+        y = (rotate16(xb[:16]) + rotate16(xb[16:])) if rotate else xb
+        ab = max(abs(v) for v in y)
+        sb = e8m0_smallest_power_at_or_above(rn32(ab / 6))
+        scale = F(2) ** (sb - 127)
+        codes = [e2m1_nearest(rn32(yi / scale)) for yi in y]
+        for k in range(16):
+            q[16 * b + k] = codes[2 * k] | (codes[2 * k + 1] << 4)
+        s[b] = sb
+    return q.reshape(rows, cols // 2), s.reshape(rows, cols // 32)

@@ -20,6 +20,7 @@
 
 uint8_t oracle_e2m1_code(float v);
 uint8_t oracle_e4m3_byte(float v);
+uint8_t oracle_e8m0_byte(float t);
 
 static const double GRID[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 
@@ -157,6 +158,36 @@ long long sweep_e4m3_linear(uint32_t lo, uint32_t hi, uint32_t stride, uint32_t 
         uint32_t u = (uint32_t)i;
         float f = from_bits(u);
         if (oracle_e4m3_byte(f) != e4m3_linear(f)) {
+            bad++;
+#pragma omp critical
+            if (u < fb)
+                fb = u;
+        }
+    }
+    *first = fb;
+    return bad;
+}
+
+/* E8M0: smallest power of two >= t, by bisection over the 255 exponents
+   -127..127 (compared exactly in double), every positive finite binary32. */
+long long sweep_e8m0_all(uint32_t *first)
+{
+    long long bad = 0;
+    uint32_t fb = 0xFFFFFFFFu;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t i = 1; i < 0x7F800000LL; i++) {
+        uint32_t u = (uint32_t)i;
+        float f = from_bits(u);
+        double t = (double)f;
+        int lo = 0, hi = 254;            /* byte b means 2^(b-127) */
+        while (lo < hi) {
+            int mid = (lo + hi) / 2;
+            if (ldexp(1.0, mid - 127) >= t)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        if (oracle_e8m0_byte(f) != (uint8_t)lo) {
             bad++;
 #pragma omp critical
             if (u < fb)

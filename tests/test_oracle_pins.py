@@ -340,7 +340,8 @@ def test_sign_of_zero_and_tiny_negatives():
     x[0, 3] = 1e-30
     q, s, g, a = oracle.quantize(x, False)
     codes = np.stack([q & 15, q >> 4], -1).reshape(-1)
-    assert codes[0] == 7 and codes[1] == 0 and codes[2] == 8 and codes[3] == 0
+    assert s[0, 0] == 98 + 127            # 2^100 / 6 rounds up to 2^98
+    assert codes[0] == 6 and codes[1] == 0 and codes[2] == 8 and codes[3] == 0
 
 
 # ---------------------------------------------------------------- P8: printed errors
@@ -468,3 +469,77 @@ def test_dequant_inverts_exactly_representable_blocks():
     q, s, g, a = oracle.quantize(x, True)
     back = oracle.dequant_f64(q, s, g, True)
     assert np.array_equal(back.reshape(-1), x.astype(np.float64).reshape(-1))
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+
+def test_e8m0_closed_forms():
+    assert oracle.e8m0_byte(0.0) == 0
+    assert oracle.e8m0_byte(1.0) == 127
+    assert oracle.e8m0_byte(float(np.nextafter(F32(1.0), F32(2.0)))) == 128
+    assert oracle.e8m0_byte(0.75) == 127
+    assert oracle.e8m0_byte(2.0 ** -127) == 0
+    assert oracle.e8m0_byte(2.0 ** -140) == 0          # clamped at 2^-127
+    assert oracle.e8m0_byte(2.0 ** 127) == 254
+    assert oracle.e8m0_byte(3.0e38) == 254             # clamped at 2^127
+    for b in range(255):
+        assert oracle.e8m0_value(b) == 2.0 ** (b - 127)
+
+
+def test_e8m0_exhaustive_against_bisection(sweeps_lib):
+    first = ctypes.c_uint32(0)
+    bad = sweeps_lib.sweep_e8m0_all(ctypes.byref(first))
+    assert bad == 0, f"{bad} mismatches, first at bits {first.value:#010x}"
+
+
+def test_mx_matches_exact_rational_model():
+    rng = np.random.default_rng(23)
+    for i in range(400):
+        rows = int(rng.integers(1, 3))
+        cols = 32 * int(rng.integers(1, 3))
+        v = rng.standard_normal(rows * cols) * np.exp2(rng.integers(-40, 40, rows * cols))
+        if i % 4 == 0:
+            v[rng.integers(0, v.size, 3)] = 0.0
+        if i % 4 == 1:
+            v = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], v.size) * \
+                np.exp2(float(rng.integers(-3, 4))) * rng.choice([-1.0, 1.0], v.size)
+        if i % 2:
+            x = v.astype(np.float32).reshape(rows, cols)
+            xf = x
+        else:
+            x = _bf16(v).reshape(rows, cols)
+            xf = synth.bf16_to_f32(x)
+        for rotate in (False, True):
+            q, s = oracle.mx_quantize(x, rotate)
+            mq, ms = em.mx_quantize(xf, rotate)
+            assert np.array_equal(q, mq) and np.array_equal(s, ms), (i, rotate)
+
+
+def test_mx_block_maximum_maps_into_3_to_6():
+    """With the smallest power of two at or above amax/6, every nonzero block's
+    largest |code| is 5, 6 or 7 (its largest value lands in (3, 6])."""
+    w = synth.make("t3_lognormal_16384x8192", rows=64)
+    for rotate in (True, False):
+        q, s = oracle.mx_quantize(w.x, rotate)
+        codes = np.stack([q & 15, q >> 4], -1).reshape(-1, 32) & 7
+        top = codes.max(1)
+        assert np.all((top >= 5) & (top <= 7))
+
+
+def test_mx_storage_is_4p25_bits_per_value():
+    x = synth.normal_bf16(256 * 64, seed=3).reshape(256, 64)
+    q, s = oracle.mx_quantize(x, True)
+    assert (q.size + s.size) / x.size == 0.53125
+
+
+def test_mx_underflow_sign_rule():
+    """A tiny negative value in a block with a huge one underflows to -0 and
+    takes code 0 (sign bit only when the quotient compares below zero)."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 2.0 ** 100
+    x[0, 1] = -(2.0 ** -140)
+    x[0, 2] = -(2.0 ** -40)
+    q, s = oracle.mx_quantize(x, False)
+    codes = np.stack([q & 15, q >> 4], -1).reshape(-1)
+    assert s[0, 0] == 98 + 127            # 2^100 / 6 rounds up to 2^98
+    assert codes[0] == 6 and codes[1] == 0 and codes[2] == 8

@@ -144,6 +144,35 @@ nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gsca
                            int64_t rows, int64_t cols, int rotate, float *y_out,
                            hipStream_t stream);
 
+/*
+ * MXFP4 variant (page "A Fused Hadamard + NVFP4 Quantization Kernel in
+ * Triton", section 1 contrasts NVFP4 with MXFP4: 32-element blocks,
+ * power-of-two E8M0 scales; its "Try this" list asks for the error study under
+ * MXFP4; the page "Hopper kernel for MXFP4" stores a scale as one byte holding
+ * a biased binary exponent, value 2^(byte - 127)).  One pass, no global scale:
+ * each 32-element block (each 16-element half rotated by H16 when rotate == 1)
+ * gets the scale 2^e with e = ceil(log2(fl(block_amax / 6))) clamped to
+ * [-127, 127] (byte 0 for an all-zero block), so the block's largest value
+ * maps into (3, 6]; each value becomes the E2M1 code of fl(y / 2^e) with the
+ * NVFP4 path's midpoint and sign rules.
+ *   x       device, row-major [rows, cols], 16-byte aligned, cols % 32 == 0.
+ *   q_out   device, rows * cols / 2 bytes, 16-byte aligned (E2M1 codes, element
+ *           2k in the low nibble of byte k).
+ *   s_out   device, rows * cols / 32 bytes: E8M0 scale bytes [rows, cols/32].
+ * Pointers may be NULL when rows * cols == 0.  Other rules as above.
+ */
+nvfp4_status mxfp4_rotquant(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,
+                            uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
+nvfp4_status mxfp4_rotquant_f32(const float *x, int64_t rows, int64_t cols, int rotate,
+                                uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
+
+/* MXFP4 dequantize: +-{0,.5,1,1.5,2,3,4,6}[code & 7] * 2^(byte - 127), rounded
+   to binary32, then each 16-element half multiplied by H16 (same butterfly and
+   * 0.25) when rotate == 1.  q: 16-byte aligned; y_out: float [rows, cols],
+   16-byte aligned; cols % 32 == 0. */
+nvfp4_status mxfp4_dequant(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols,
+                           int rotate, float *y_out, hipStream_t stream);
+
 /* Static English text for a status code; never NULL. */
 const char *nvfp4_status_string(nvfp4_status status);
 

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "Nvfp4Error", "rotquant", "rotamax", "quant_from_amax", "dequant",
-    "status_string", "lib",
+    "status_string", "lib", "mx_rotquant", "mx_dequant",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +44,9 @@ _SIGS = {
     "nvfp4_quant_from_amax": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_quant_from_amax_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_dequant": [_p, _p, _p, _i64, _i64, _int, _p, _p],
+    "mxfp4_rotquant": [_p, _i64, _i64, _int, _p, _p, _p],
+    "mxfp4_rotquant_f32": [_p, _i64, _i64, _int, _p, _p, _p],
+    "mxfp4_dequant": [_p, _p, _i64, _i64, _int, _p, _p],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -159,4 +162,31 @@ def dequant(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = Tr
     _check("nvfp4_dequant", lib.nvfp4_dequant(_ptr(q), _ptr(s), _ptr(g), rows, cols,
                                               int(bool(rotate)), _ptr(out),
                                               _stream(q.device, stream)))
+    return out
+
+
+def mx_rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, stream=None):
+    """MXFP4 single pass.  x: bfloat16 or float32 [rows, cols], cols % 32 == 0.
+    Returns (q uint8 [rows, cols/2], s uint8 [rows, cols/32] E8M0 bytes)."""
+    rows, cols = _check_input(x)
+    if out is None:
+        q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+        s = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)
+    else:
+        q, s = out
+    fn = _variant(x, "mxfp4_rotquant")
+    _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(q), _ptr(s),
+                                _stream(x.device, stream)))
+    return q, s
+
+
+def mx_dequant(q: torch.Tensor, s: torch.Tensor, rotate: bool = True,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    rows, cols = s.shape[0], s.shape[1] * 32
+    if q.shape != (rows, cols // 2):
+        raise ValueError("q and s shapes disagree")
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.float32, device=q.device)
+    _check("mxfp4_dequant", lib.mxfp4_dequant(_ptr(q), _ptr(s), rows, cols, int(bool(rotate)),
+                                              _ptr(out), _stream(q.device, stream)))
     return out

@@ -328,6 +328,103 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   }
 }
 
+
+// ---------------------------------------------------------------- MXFP4 variant
+
+// MXFP4 (the contrast format of section 1 of the page: 32-element blocks,
+// power-of-two E8M0 scales; the page "Hopper kernel for MXFP4" stores a scale
+// as a biased exponent byte, value 2^(byte - 127)).  There is no global scale,
+// so this is a single pass: each lane rotates (each 16-element half with H16),
+// scales and encodes one 32-element block per iteration.  Readings: the scale
+// is the smallest power of two at or above fl(block_amax / 6), exponent
+// clamped to [-127, 127], 0 for an all-zero block; v = fl(y / scale), which
+// is the exact product y * 2^-e rounded once; then the E2M1 rule of the NVFP4
+// path (+0.0 turns an underflowed -0.0 into +0.0: code 0, not 8).
+template <typename T, bool ROTATE>
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(const T* __restrict__ x, int64_t nb32,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ s) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb32; b += stride) {
+    float v[4][8];     // halves: (v[0], v[1]) elements 0..15, (v[2], v[3]) 16..31
+    load_block(x, 2 * b, v[0], v[1]);
+    load_block(x, 2 * b + 1, v[2], v[3]);
+    if (ROTATE) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        stages_1_2_4(v[2 * h]);
+        stages_1_2_4(v[2 * h + 1]);
+        stage_8(v[2 * h], v[2 * h + 1]);
+      }
+    }
+    float az = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) az = __builtin_fmaxf(az, __builtin_fabsf(v[k][i]));
+    const float t = (ROTATE ? 0.25f * az : az) / 6.0f;
+    int e = -127;
+    if (t > 0.0f) {
+      int fe;
+      const float m = frexpf(t, &fe);          // t = m 2^fe, m in [0.5, 1)
+      e = m == 0.5f ? fe - 1 : fe;             // ceil(log2 t)
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    // bf16: the butterfly output z = 4y is exact and y * 2^-e = z * 2^(-e-2);
+    // fp32 values may round when scaled by 0.25, so they are scaled first.
+    const bool fold = ROTATE && sizeof(T) == 2;
+    const float inv = ldexpf(1.0f, fold ? -e - 2 : -e);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float y = (ROTATE && !fold) ? 0.25f * v[k][i] : v[k][i];
+        v[k][i] = y * inv + 0.0f;
+      }
+    *reinterpret_cast<uint4*>(q + b * 16) =
+        make_uint4(e2m1_pack8(v[0]), e2m1_pack8(v[1]), e2m1_pack8(v[2]), e2m1_pack8(v[3]));
+    s[b] = static_cast<uint8_t>(e + 127);
+  }
+}
+
+// MXFP4 dequantize: +-GRID[c & 7] * 2^(byte - 127), rounded to binary32, then
+// the inverse rotation of each half (the same butterfly and * 0.25).
+__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ q,
+                                                              const uint8_t* __restrict__ s,
+                                                              int64_t nb32, int rotate,
+                                                              float* __restrict__ y) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb32; b += stride) {
+    const uint4 w = *reinterpret_cast<const uint4*>(q + b * 16);
+    const float sc = ldexpf(1.0f, static_cast<int>(s[b]) - 127);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    float v[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[k][i] = e2m1_value((ww[k] >> (4 * i)) & 15u) * sc;
+    if (rotate) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        stages_1_2_4(v[2 * h]);
+        stages_1_2_4(v[2 * h + 1]);
+        stage_8(v[2 * h], v[2 * h + 1]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[2 * h][i] = 0.25f * v[2 * h][i];
+          v[2 * h + 1][i] = 0.25f * v[2 * h + 1][i];
+        }
+      }
+    }
+    float4* o = reinterpret_cast<float4*>(y + b * 32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
+      o[2 * k + 1] = make_float4(v[k][4], v[k][5], v[k][6], v[k][7]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host helpers
 
 // hipLaunchKernel with the kernel's own parameter types; returns the launch status.
@@ -513,6 +610,29 @@ nvfp4_status quant_from_amax(const T* x, int64_t rows, int64_t cols, int rotate,
   return enqueue_quant(x, nb, rotate, amax, q, s, g, st);
 }
 
+
+template <typename T>
+nvfp4_status mx_rotquant(const T* x, int64_t rows, int64_t cols, int rotate, uint8_t* q, uint8_t* s,
+                         hipStream_t st) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  int64_t nb = 0;
+  nvfp4_status r = check_shape(rows, cols, &nb);
+  if (r != NVFP4_OK) return r;
+  const int64_t n = rows * cols;
+  if (n != 0 && (!x || !q || !s)) return NVFP4_ERR_NULL;
+  if (rotate != 0 && rotate != 1) return NVFP4_ERR_ARG;
+  if (n != 0 && (!aligned(x, 16) || !aligned(q, 16))) return NVFP4_ERR_ALIGN;
+  const Range rx = range_of(x, n * static_cast<int64_t>(sizeof(T)));
+  const Range rq = range_of(q, n / 2), rs = range_of(s, n / 32);
+  if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return NVFP4_ERR_ARG;
+  const int64_t nb32 = n / 32;
+  if (nb32 == 0) return NVFP4_OK;
+  const dim3 grid(quant_grid(nb32));
+  const hipError_t e = rotate ? launch(mx_quant_kernel<T, true>, grid, dim3(kThreads), st, x, nb32, q, s)
+                              : launch(mx_quant_kernel<T, false>, grid, dim3(kThreads), st, x, nb32, q, s);
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -569,6 +689,36 @@ nvfp4_status nvfp4_dequant(const uint8_t* q, const uint8_t* s, const float* gsca
     return NVFP4_ERR_ARG;
   if (nb == 0) return NVFP4_OK;
   if (launch(dequant_kernel, dim3(generic_grid(nb)), dim3(kThreads), stream, q, s, gscale, nb, rotate,
+             y_out) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  return NVFP4_OK;
+}
+
+nvfp4_status mxfp4_rotquant(const uint16_t* x_bf16, int64_t rows, int64_t cols, int rotate,
+                            uint8_t* q_out, uint8_t* s_out, hipStream_t stream) {
+  return mx_rotquant(x_bf16, rows, cols, rotate, q_out, s_out, stream);
+}
+
+nvfp4_status mxfp4_rotquant_f32(const float* x, int64_t rows, int64_t cols, int rotate,
+                                uint8_t* q_out, uint8_t* s_out, hipStream_t stream) {
+  return mx_rotquant(x, rows, cols, rotate, q_out, s_out, stream);
+}
+
+nvfp4_status mxfp4_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
+                           int rotate, float* y_out, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  int64_t nb = 0;
+  nvfp4_status r = check_shape(rows, cols, &nb);
+  if (r != NVFP4_OK) return r;
+  const int64_t n = rows * cols;
+  if (n != 0 && (!q || !s || !y_out)) return NVFP4_ERR_NULL;
+  if (rotate != 0 && rotate != 1) return NVFP4_ERR_ARG;
+  if (n != 0 && (!aligned(q, 16) || !aligned(y_out, 16))) return NVFP4_ERR_ALIGN;
+  const Range ry = range_of(y_out, n * 4);
+  if (overlap(ry, range_of(q, n / 2)) || overlap(ry, range_of(s, n / 32))) return NVFP4_ERR_ARG;
+  const int64_t nb32 = n / 32;
+  if (nb32 == 0) return NVFP4_OK;
+  if (launch(mx_dequant_kernel, dim3(generic_grid(nb32)), dim3(kThreads), stream, q, s, nb32, rotate,
              y_out) != hipSuccess)
     return NVFP4_ERR_HIP;
   return NVFP4_OK;

@@ -70,6 +70,7 @@ def _load():
     lib.oracle_mx_quantize.restype = _int
     lib.oracle_mx_roundtrip_error.argtypes = [_ptr, _int, _i64, _i64, _int, _ptr, _ptr, _int]
     lib.oracle_mx_roundtrip_error.restype = ctypes.c_double
+    lib.oracle_mx_dequant_f64.argtypes = [_ptr, _ptr, _i64, _i64, _int, _ptr, _int]
     lib.oracle_e4m3_byte_bits.argtypes = [_u32, _u32, _ptr, _int]
     _lib = lib
     return lib
@@ -228,3 +229,12 @@ def mx_roundtrip_error(x: np.ndarray, rotate: bool, q: np.ndarray, s: np.ndarray
     return float(_load().oracle_mx_roundtrip_error(
         _p(x), _is_f32(x), rows, cols, int(rotate), _p(np.ascontiguousarray(q)),
         _p(np.ascontiguousarray(s)), nthreads))
+
+
+def mx_dequant_f64(q: np.ndarray, s: np.ndarray, rotate: bool, nthreads: int = 0) -> np.ndarray:
+    rows = s.shape[0]
+    cols = s.shape[1] * 32
+    out = np.empty((rows, cols), dtype=np.float64)
+    _load().oracle_mx_dequant_f64(_p(np.ascontiguousarray(q)), _p(np.ascontiguousarray(s)),
+                                  rows, cols, int(rotate), _p(out), nthreads)
+    return out

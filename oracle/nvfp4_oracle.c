@@ -565,6 +565,48 @@ int oracle_mx_quantize(const void *x, int is_f32, int64_t rows, int64_t cols, in
     return 0;
 }
 
+/* Decode of one MX block to fp64: +-GRID[c & 7] * scale (exact), then the exact
+   inverse rotation H16 / 4 of each half (H16 is its own inverse up to 1/16). */
+static void mx_decode_block(const uint8_t *q16, uint8_t sb, int rotate, double *out)
+{
+    double scale = (double)oracle_e8m0_value(sb);
+    double yh[32];
+    for (int i = 0; i < 32; i++) {
+        int c = (i & 1) ? (q16[i / 2] >> 4) : (q16[i / 2] & 15);
+        double mag = E2M1_GRID[c & 7] * scale;
+        yh[i] = (c & 8) ? -mag : mag;
+    }
+    for (int h = 0; h < 2; h++) {
+        for (int i = 0; i < 16; i++) {
+            if (!rotate) {
+                out[16 * h + i] = yh[16 * h + i];
+                continue;
+            }
+            double acc = 0.0;
+            for (int j = 0; j < 16; j++) {
+                int sign = __builtin_popcount((unsigned)(i & j)) & 1;
+                acc += (sign ? -yh[16 * h + j] : yh[16 * h + j]) * 0.25;
+            }
+            out[16 * h + i] = acc;
+        }
+    }
+}
+
+/* fp64 decode of a whole MXFP4 tensor into out [rows, cols]. */
+void oracle_mx_dequant_f64(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols,
+                           int rotate, double *out, int nthreads)
+{
+    int64_t nb = rows * (cols / 32);
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+#endif
+    for (int64_t b = 0; b < nb; b++)
+        mx_decode_block(q + 16 * b, s[b], rotate, out + 32 * b);
+    (void)nthreads;
+}
+
 /* Relative L2 round-trip error of an MXFP4 encoding (fp64 sums, exact H). */
 double oracle_mx_roundtrip_error(const void *x, int is_f32, int64_t rows, int64_t cols,
                                  int rotate, const uint8_t *q, const uint8_t *s, int nthreads)
@@ -579,28 +621,8 @@ double oracle_mx_roundtrip_error(const void *x, int is_f32, int64_t rows, int64_
     for (int64_t b = 0; b < nb; b++) {
         float xb[32];
         load_span(x, is_f32, b * 32, 32, xb);
-        float scale = oracle_e8m0_value(s[b]);
-        double yh[32], xh[32];
-        for (int i = 0; i < 32; i++) {
-            int c = (i & 1) ? (q[16 * b + i / 2] >> 4) : (q[16 * b + i / 2] & 15);
-            float mag = (float)E2M1_GRID[c & 7];
-            float val = (c & 8) ? -mag : mag;
-            yh[i] = (double)(val * scale);
-        }
-        for (int h = 0; h < 2; h++) {
-            for (int i = 0; i < 16; i++) {
-                if (!rotate) {
-                    xh[16 * h + i] = yh[16 * h + i];
-                    continue;
-                }
-                double acc = 0.0;
-                for (int j = 0; j < 16; j++) {
-                    int sign = __builtin_popcount((unsigned)(i & j)) & 1;
-                    acc += (sign ? -yh[16 * h + j] : yh[16 * h + j]) * 0.25;
-                }
-                xh[16 * h + i] = acc;
-            }
-        }
+        double xh[32];
+        mx_decode_block(q + 16 * b, s[b], rotate, xh);
         for (int i = 0; i < 32; i++) {
             double d = xh[i] - (double)xb[i];
             num += d * d;

@@ -20,7 +20,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ARG, ERR_HIP = range(6)
 def declared_functions() -> list[str]:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:nvfp4|mxfp4)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -33,6 +33,9 @@ def lib():
     for name in ("nvfp4_rotamax", "nvfp4_rotamax_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, i, p, p]
     lib.nvfp4_dequant.argtypes = [p, p, p, i64, i64, i, p, p]
+    for name in ("mxfp4_rotquant", "mxfp4_rotquant_f32"):
+        getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p]
+    lib.mxfp4_dequant.argtypes = [p, p, i64, i64, i, p, p]
     lib.nvfp4_status_string.argtypes = [i]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     return lib
@@ -41,7 +44,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("nvfp4_rotquant", "nvfp4_rotquant_f32", "nvfp4_dequant",
-                 "nvfp4_status_string", "nvfp4_rotamax", "nvfp4_quant_from_amax"):
+                 "nvfp4_status_string", "nvfp4_rotamax", "nvfp4_quant_from_amax",
+                 "mxfp4_rotquant", "mxfp4_rotquant_f32", "mxfp4_dequant"):
         assert must in names
 
 
@@ -125,3 +129,35 @@ def test_dequant_validation(lib):
     assert f(Q + 4, S, G, 4, 64, 1, Y, None) == ERR_ALIGN
     assert f(Q, S, G, 4, 64, 1, Y + 8, None) == ERR_ALIGN
     assert f(Q, S, G, 4, 64, 1, Q, None) == ERR_ARG
+
+
+@pytest.mark.parametrize("name", ["mxfp4_rotquant", "mxfp4_rotquant_f32"])
+def test_mx_quant_validation(lib, name):
+    f = lambda x=X, rows=4, cols=64, rotate=1, q=Q, s=S: getattr(lib, name)(  # noqa: E731
+        x, rows, cols, rotate, q, s, None)
+    assert f(x=None) == ERR_NULL
+    assert f(q=None) == ERR_NULL
+    assert f(s=None) == ERR_NULL
+    assert f(cols=48) == ERR_SHAPE          # a multiple of 16, not of 32
+    assert f(cols=-32) == ERR_SHAPE
+    assert f(rows=-1) == ERR_SHAPE
+    assert f(rows=1 << 40, cols=1 << 40) == ERR_SHAPE
+    assert f(rotate=2) == ERR_ARG
+    assert f(x=X + 8) == ERR_ALIGN
+    assert f(q=Q + 8) == ERR_ALIGN
+    assert f(q=X) == ERR_ARG
+    assert f(s=Q + 16) == ERR_ARG
+    assert f(x=None, q=None, s=None, rows=0) == OK     # empty: nothing to do
+
+
+def test_mx_dequant_validation(lib):
+    f = lib.mxfp4_dequant
+    Y = 0x80000
+    assert f(None, S, 4, 64, 1, Y, None) == ERR_NULL
+    assert f(Q, None, 4, 64, 1, Y, None) == ERR_NULL
+    assert f(Q, S, 4, 64, 1, None, None) == ERR_NULL
+    assert f(Q, S, 4, 48, 1, Y, None) == ERR_SHAPE
+    assert f(Q, S, 4, 64, 5, Y, None) == ERR_ARG
+    assert f(Q + 4, S, 4, 64, 1, Y, None) == ERR_ALIGN
+    assert f(Q, S, 4, 64, 1, Y + 8, None) == ERR_ALIGN
+    assert f(Q, S, 4, 64, 1, Q, None) == ERR_ARG

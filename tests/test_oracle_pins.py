@@ -543,3 +543,24 @@ def test_mx_underflow_sign_rule():
     codes = np.stack([q & 15, q >> 4], -1).reshape(-1)
     assert s[0, 0] == 98 + 127            # 2^100 / 6 rounds up to 2^98
     assert codes[0] == 6 and codes[1] == 0 and codes[2] == 8
+
+
+def test_mx_dequant_inverts_exactly_representable_blocks():
+    """Two 16-element halves whose (rotated) values are E2M1 grid points times
+    2^k, with a largest magnitude of 6 * 2^k, so the block scale is exactly
+    2^k: encode then decode returns the input exactly, for either rotation
+    setting and for scales from 2^-120 to 2^120."""
+    t = np.array([6, -4, 3, 2, -1.5, 1, 0.5, 0, -6, 4, -3, 2, 1.5, -1, 0.5, 0,
+                  0.5, 6, -0.5, 1, 1.5, -2, 3, -4, 0, 0, 1, -1, 2, -2, 4, -3],
+                 dtype=np.float64)
+    H = sylvester16()
+    for k in (-120, -7, 0, 5, 120):
+        for rotate in (False, True):
+            y = t * 2.0 ** k
+            x = np.concatenate([H @ y[:16], H @ y[16:]]) if rotate else y
+            x32 = x.astype(np.float32).reshape(1, 32)
+            assert np.array_equal(x32.astype(np.float64).reshape(-1), x)   # exact input
+            q, s = oracle.mx_quantize(x32, rotate)
+            assert s[0, 0] == k + 127
+            back = oracle.mx_dequant_f64(q, s, rotate)
+            assert np.array_equal(back.reshape(-1), x), (k, rotate)

@@ -226,6 +226,50 @@ def main() -> int:
     p2 = statistics.mean(p2_ms)
     p2_gbs = nbytes["pass2"] / (p2 * 1e-3) / 1e9
 
+    def timed(fn):
+        """Mean event interval of fn over K cold steps (context figures)."""
+        fn()
+        evs = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if not args.no_flush:
+                cold()
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return statistics.mean(u.elapsed_time(v) for u, v in evs)
+
+    # Context: MXFP4 single pass (32-element blocks, E8M0 scales, no global
+    # scale): reads 2 B and writes 0.5 + 1/32 B per element.
+    qm = torch.empty(ROWS, COLS // 2, dtype=torch.uint8, device=dev)
+    sm = torch.empty(ROWS, COLS // 32, dtype=torch.uint8, device=dev)
+    mx_ms = timed(lambda: nv.mx_rotquant(x, rotate=True, out=(qm, sm)))
+    mx_bytes = 2 * n + n // 2 + n // 32
+
+    # Context: the unfused three-kernel arrangement (rotate to fp32 in HBM,
+    # amax over it, quantize it with rotation off); same output bytes.
+    y32 = torch.empty(ROWS, COLS, dtype=torch.float32, device=dev)
+    qu = torch.empty_like(q)
+    su = torch.empty_like(s)
+    gu = torch.empty_like(g)
+    au = torch.empty_like(a)
+
+    def unfused():
+        nv.rotate16(x, out=y32)
+        nv.rotamax(y32, rotate=False, amax=au)
+        nv.quant_from_amax(y32, au, rotate=False, out=(qu, su, gu))
+    unfused_ms = timed(unfused)
+    unfused_bytes = 2 * n + 4 * n + 4 * n + 4 * n + n // 2 + n // 16 + 8
+    unfused_same = bool(torch.equal(qu, q) and torch.equal(su, s) and torch.equal(gu, g))
+
+    # Context: decode (codes + scales + g in, fp32 out, inverse rotation).
+    yd = nv.dequant(q, s, g, rotate=True)
+    dq_ms = timed(lambda: nv.dequant(q, s, g, rotate=True, out=yd))
+    dq_bytes = n // 2 + n // 16 + 4 + 4 * n
+    del y32, yd
+
     # parity spot check of the timed outputs against a second call (cheap)
     q2, s2, g2, a2 = nv.rotquant(x, rotate=True)
     torch.cuda.synchronize()
@@ -265,6 +309,15 @@ def main() -> int:
                      "frac": round(p2_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes["pass2"]},
+        "mxfp4_single_pass": {"ms": round(mx_ms, 5), "bytes_per_elem": mx_bytes / n,
+                              "gbs": round(mx_bytes / (mx_ms * 1e-3) / 1e9, 2)},
+        "unfused_three_kernel": {"ms": round(unfused_ms, 5),
+                                 "algorithmic_bytes_per_elem": round(unfused_bytes / n, 4),
+                                 "gbs": round(unfused_bytes / (unfused_ms * 1e-3) / 1e9, 2),
+                                 "fused_speedup": round(unfused_ms / ms, 3),
+                                 "same_bytes_as_fused": unfused_same},
+        "dequant": {"ms": round(dq_ms, 5), "bytes_per_elem": round(dq_bytes / n, 4),
+                    "gbs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 2)},
         "timed_wall_s": round(wall, 4),
         "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "graph_replay_gbs": None if graph_ms is None else round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 2),

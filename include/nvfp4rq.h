@@ -145,6 +145,23 @@ nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gsca
                            hipStream_t stream);
 
 /*
+ * Rotation alone: y = x H16 on every 16-element block (butterfly with strides
+ * 1, 2, 4, 8, then * 0.25; the arithmetic of nvfp4_rotquant's rotation), stored
+ * as fp32 [rows, cols].  With nvfp4_rotamax_f32 and nvfp4_quant_from_amax_f32
+ * (rotate = 0) on y it forms the unfused three-kernel arrangement the page "A
+ * Fused Hadamard + NVFP4 Quantization Kernel in Triton" sets against the fused
+ * kernel (opening paragraph; "Try this" item 4); those outputs equal
+ * nvfp4_rotquant's byte for byte.  H16 / 4 is its own inverse, so the call also
+ * undoes a rotation up to rounding.
+ *   x      device, [rows, cols], 16-byte aligned, cols % 16 == 0.
+ *   y_out  device fp32 [rows, cols], 16-byte aligned, not overlapping x.
+ */
+nvfp4_status nvfp4_rotate16(const uint16_t *x_bf16, int64_t rows, int64_t cols, float *y_out,
+                            hipStream_t stream);
+nvfp4_status nvfp4_rotate16_f32(const float *x, int64_t rows, int64_t cols, float *y_out,
+                                hipStream_t stream);
+
+/*
  * MXFP4 variant (page "A Fused Hadamard + NVFP4 Quantization Kernel in
  * Triton", section 1 contrasts NVFP4 with MXFP4: 32-element blocks,
  * power-of-two E8M0 scales; its "Try this" list asks for the error study under

@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "LIB_PATH", "Nvfp4Error", "rotquant", "rotamax", "quant_from_amax", "dequant",
     "status_string", "lib", "mx_rotquant", "mx_dequant",
+    "rotate16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +45,8 @@ _SIGS = {
     "nvfp4_quant_from_amax": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_quant_from_amax_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_dequant": [_p, _p, _p, _i64, _i64, _int, _p, _p],
+    "nvfp4_rotate16": [_p, _i64, _i64, _p, _p],
+    "nvfp4_rotate16_f32": [_p, _i64, _i64, _p, _p],
     "mxfp4_rotquant": [_p, _i64, _i64, _int, _p, _p, _p],
     "mxfp4_rotquant_f32": [_p, _i64, _i64, _int, _p, _p, _p],
     "mxfp4_dequant": [_p, _p, _i64, _i64, _int, _p, _p],
@@ -162,6 +165,16 @@ def dequant(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = Tr
     _check("nvfp4_dequant", lib.nvfp4_dequant(_ptr(q), _ptr(s), _ptr(g), rows, cols,
                                               int(bool(rotate)), _ptr(out),
                                               _stream(q.device, stream)))
+    return out
+
+
+def rotate16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The block rotation alone: float32 [rows, cols] = x H16 per 16-element block."""
+    rows, cols = _check_input(x)
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.float32, device=x.device)
+    fn = _variant(x, "nvfp4_rotate16")
+    _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, _ptr(out), _stream(x.device, stream)))
     return out
 
 

@@ -329,6 +329,32 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 }
 
 
+
+// ---------------------------------------------------------------- rotation alone
+
+// y = x H16 per 16-element block (butterfly, then * 0.25), stored as fp32.
+// The first kernel of the unfused three-kernel arrangement that the page
+// "A Fused Hadamard + NVFP4 Quantization Kernel in Triton" compares the fused
+// kernel against (opening paragraph; "Try this" item 4): rotated values go to
+// HBM and the amax and quantize kernels read them back with rotation off.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rotate_kernel(const T* __restrict__ x, int64_t nb,
+                                                          float* __restrict__ y) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb; b += stride) {
+    float lo[8], hi[8];
+    load_block(x, b, lo, hi);
+    stages_1_2_4(lo);
+    stages_1_2_4(hi);
+    stage_8(lo, hi);
+    float4* o = reinterpret_cast<float4*>(y + b * 16);
+    o[0] = make_float4(0.25f * lo[0], 0.25f * lo[1], 0.25f * lo[2], 0.25f * lo[3]);
+    o[1] = make_float4(0.25f * lo[4], 0.25f * lo[5], 0.25f * lo[6], 0.25f * lo[7]);
+    o[2] = make_float4(0.25f * hi[0], 0.25f * hi[1], 0.25f * hi[2], 0.25f * hi[3]);
+    o[3] = make_float4(0.25f * hi[4], 0.25f * hi[5], 0.25f * hi[6], 0.25f * hi[7]);
+  }
+}
+
 // ---------------------------------------------------------------- MXFP4 variant
 
 // MXFP4 (the contrast format of section 1 of the page: 32-element blocks,
@@ -633,6 +659,22 @@ nvfp4_status mx_rotquant(const T* x, int64_t rows, int64_t cols, int rotate, uin
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+
+template <typename T>
+nvfp4_status rotate_only(const T* x, int64_t rows, int64_t cols, float* y, hipStream_t st) {
+  int64_t nb = 0;
+  nvfp4_status r = check_shape(rows, cols, &nb);
+  if (r != NVFP4_OK) return r;
+  const int64_t n = rows * cols;
+  if (n != 0 && (!x || !y)) return NVFP4_ERR_NULL;
+  if (n != 0 && (!aligned(x, 16) || !aligned(y, 16))) return NVFP4_ERR_ALIGN;
+  if (overlap(range_of(x, n * static_cast<int64_t>(sizeof(T))), range_of(y, n * 4)))
+    return NVFP4_ERR_ARG;
+  if (nb == 0) return NVFP4_OK;
+  return launch(rotate_kernel<T>, dim3(generic_grid(nb)), dim3(kThreads), st, x, nb, y) == hipSuccess
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -692,6 +734,16 @@ nvfp4_status nvfp4_dequant(const uint8_t* q, const uint8_t* s, const float* gsca
              y_out) != hipSuccess)
     return NVFP4_ERR_HIP;
   return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_rotate16(const uint16_t* x_bf16, int64_t rows, int64_t cols, float* y_out,
+                            hipStream_t stream) {
+  return rotate_only(x_bf16, rows, cols, y_out, stream);
+}
+
+nvfp4_status nvfp4_rotate16_f32(const float* x, int64_t rows, int64_t cols, float* y_out,
+                                hipStream_t stream) {
+  return rotate_only(x, rows, cols, y_out, stream);
 }
 
 nvfp4_status mxfp4_rotquant(const uint16_t* x_bf16, int64_t rows, int64_t cols, int rotate,

@@ -70,6 +70,8 @@ def _load():
     lib.oracle_mx_quantize.restype = _int
     lib.oracle_mx_roundtrip_error.argtypes = [_ptr, _int, _i64, _i64, _int, _ptr, _ptr, _int]
     lib.oracle_mx_roundtrip_error.restype = ctypes.c_double
+    lib.oracle_rotate_tensor.argtypes = [_ptr, _int, _i64, _i64, _ptr, _int]
+    lib.oracle_rotate_tensor.restype = _int
     lib.oracle_mx_dequant_f64.argtypes = [_ptr, _ptr, _i64, _i64, _int, _ptr, _int]
     lib.oracle_e4m3_byte_bits.argtypes = [_u32, _u32, _ptr, _int]
     _lib = lib
@@ -96,6 +98,15 @@ def rotate16(x: np.ndarray) -> np.ndarray:
     xi = np.ascontiguousarray(x, dtype=np.float32).reshape(16)
     y = np.empty(16, dtype=np.float32)
     _load().oracle_rotate16(_p(xi), _p(y))
+    return y
+
+
+def rotate_tensor(x: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """rotate16 applied to every 16-element block of x [rows, cols]; float32."""
+    rows, cols = x.shape
+    y = np.empty((rows, cols), dtype=np.float32)
+    if _load().oracle_rotate_tensor(_p(x), _is_f32(x), rows, cols, _p(y), nthreads):
+        raise ValueError("cols must be a multiple of 16")
     return y
 
 

@@ -632,3 +632,30 @@ double oracle_mx_roundtrip_error(const void *x, int is_f32, int64_t rows, int64_
     (void)nthreads;
     return sqrt(num) / sqrt(den);
 }
+
+/* ------------------------------------------------------------------ */
+/* Rotation of a whole tensor (the first kernel of the unfused        */
+/* three-kernel arrangement)                                          */
+/* ------------------------------------------------------------------ */
+
+/* y [rows, cols] fp32 = oracle_rotate16 of every 16-element block of x.
+   Returns 0, or -1 on a bad shape. */
+int oracle_rotate_tensor(const void *x, int is_f32, int64_t rows, int64_t cols, float *y,
+                         int nthreads)
+{
+    if (cols % 16 != 0 || rows < 0 || cols < 0)
+        return -1;
+    int64_t nb = rows * (cols / 16);
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+#endif
+    for (int64_t b = 0; b < nb; b++) {
+        float xb[16];
+        load_span(x, is_f32, b * 16, 16, xb);
+        oracle_rotate16(xb, y + 16 * b);
+    }
+    (void)nthreads;
+    return 0;
+}

@@ -36,6 +36,8 @@ def lib():
     for name in ("mxfp4_rotquant", "mxfp4_rotquant_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p]
     lib.mxfp4_dequant.argtypes = [p, p, i64, i64, i, p, p]
+    for name in ("nvfp4_rotate16", "nvfp4_rotate16_f32"):
+        getattr(lib, name).argtypes = [p, i64, i64, p, p]
     lib.nvfp4_status_string.argtypes = [i]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     return lib
@@ -45,7 +47,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("nvfp4_rotquant", "nvfp4_rotquant_f32", "nvfp4_dequant",
                  "nvfp4_status_string", "nvfp4_rotamax", "nvfp4_quant_from_amax",
-                 "mxfp4_rotquant", "mxfp4_rotquant_f32", "mxfp4_dequant"):
+                 "mxfp4_rotquant", "mxfp4_rotquant_f32", "mxfp4_dequant",
+                 "nvfp4_rotate16", "nvfp4_rotate16_f32"):
         assert must in names
 
 
@@ -161,3 +164,16 @@ def test_mx_dequant_validation(lib):
     assert f(Q + 4, S, 4, 64, 1, Y, None) == ERR_ALIGN
     assert f(Q, S, 4, 64, 1, Y + 8, None) == ERR_ALIGN
     assert f(Q, S, 4, 64, 1, Q, None) == ERR_ARG
+
+
+@pytest.mark.parametrize("name", ["nvfp4_rotate16", "nvfp4_rotate16_f32"])
+def test_rotate_validation(lib, name):
+    f = getattr(lib, name)
+    Y = 0x80000
+    assert f(None, 4, 64, Y, None) == ERR_NULL
+    assert f(X, 4, 64, None, None) == ERR_NULL
+    assert f(X, 4, 40, Y, None) == ERR_SHAPE
+    assert f(X + 8, 4, 64, Y, None) == ERR_ALIGN
+    assert f(X, 4, 64, Y + 4, None) == ERR_ALIGN
+    assert f(X, 4, 64, X + 64, None) == ERR_ARG
+    assert f(None, 0, 64, None, None) == OK

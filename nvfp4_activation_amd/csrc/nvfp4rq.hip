@@ -290,45 +290,68 @@ __global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict_
   quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s);
 }
 
+// Kernels that write fp32 per element (decode, rotation alone) use a
+// quarter-block layout: a wave takes 64 * kQuarters consecutive 4-element
+// quarters per iteration, lane l quarters l, l + 64, ..., so that every store
+// instruction of the wave writes 1 KiB of consecutive outputs.  A block's four
+// quarters sit in the four lanes of a quad; strides 1 and 2 of the butterfly
+// run in lane, strides 4 and 8 through quad lane exchanges.  The tail
+// iteration is wave-uniform and every lane runs the exchanges; only the loads
+// and stores are predicated.
+constexpr int kQuarters = 8;
+
+__device__ __forceinline__ void load_quarter(const float* __restrict__ x, int64_t pc, float z[4]) {
+  const float4 v = reinterpret_cast<const float4*>(x)[pc];
+  z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
+}
+
+__device__ __forceinline__ void load_quarter(const uint16_t* __restrict__ x, int64_t pc,
+                                             float z[4]) {
+  const uint2 v = reinterpret_cast<const uint2*>(x)[pc];
+  z[0] = bf16_lo(v.x); z[1] = bf16_hi(v.x); z[2] = bf16_lo(v.y); z[3] = bf16_hi(v.y);
+}
+
 // Dequantize (section 2, dequantize): +-GRID[c & 7] * RN(float(s) * g), then
 // the same butterfly and * 0.25 when rotated (H16 is symmetric, so H16^T is
-// the forward transform).
+// the forward transform).  nq = number of quarters = rows * cols / 4.
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ s,
                                                            const float* __restrict__ gscale,
-                                                           int64_t nb, int rotate,
+                                                           int64_t nq, int rotate,
                                                            float* __restrict__ y) {
+  const uint32_t lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  constexpr int64_t kPerWave = 64 * kQuarters;
+  const uint16_t* __restrict__ q2 = reinterpret_cast<const uint16_t*>(q);  // 4 codes
+  float4* __restrict__ o = reinterpret_cast<float4*>(y);
   const float g = *gscale;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb;
-       b += stride) {
-    const uint2 w = *reinterpret_cast<const uint2*>(q + b * 8);
-    const float sf = e4m3_value(s[b]) * g;
-    float lo[8], hi[8];
+  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
+    uint32_t c[kQuarters], sb[kQuarters];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo[i] = e2m1_value((w.x >> (4 * i)) & 15u) * sf;
-      hi[i] = e2m1_value((w.y >> (4 * i)) & 15u) * sf;
+    for (int j = 0; j < kQuarters; ++j) {
+      const int64_t pc = base + j * 64 + lane;
+      const bool in = pc < nq;
+      c[j] = in ? q2[pc] : 0u;
+      sb[j] = in ? s[pc >> 2] : 0u;
     }
-    if (rotate) {
-      stages_1_2_4(lo);
-      stages_1_2_4(hi);
-      stage_8(lo, hi);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo[i] = 0.25f * lo[i];
-        hi[i] = 0.25f * hi[i];
+    for (int j = 0; j < kQuarters; ++j) {
+      const float sf = e4m3_value(sb[j]) * g;
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = e2m1_value((c[j] >> (4 * i)) & 15u) * sf;
+      if (rotate) {
+        stages_1_2(z);
+        quad_stages_4_8(z, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = 0.25f * z[i];
       }
+      const int64_t pc = base + j * 64 + lane;
+      if (pc < nq) o[pc] = make_float4(z[0], z[1], z[2], z[3]);
     }
-    float4* o = reinterpret_cast<float4*>(y + b * 16);
-    o[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
-    o[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
-    o[2] = make_float4(hi[0], hi[1], hi[2], hi[3]);
-    o[3] = make_float4(hi[4], hi[5], hi[6], hi[7]);
   }
 }
-
-
 
 // ---------------------------------------------------------------- rotation alone
 
@@ -338,20 +361,38 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 // kernel against (opening paragraph; "Try this" item 4): rotated values go to
 // HBM and the amax and quantize kernels read them back with rotation off.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void rotate_kernel(const T* __restrict__ x, int64_t nb,
+__global__ __launch_bounds__(kThreads) void rotate_kernel(const T* __restrict__ x, int64_t nq,
                                                           float* __restrict__ y) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb; b += stride) {
-    float lo[8], hi[8];
-    load_block(x, b, lo, hi);
-    stages_1_2_4(lo);
-    stages_1_2_4(hi);
-    stage_8(lo, hi);
-    float4* o = reinterpret_cast<float4*>(y + b * 16);
-    o[0] = make_float4(0.25f * lo[0], 0.25f * lo[1], 0.25f * lo[2], 0.25f * lo[3]);
-    o[1] = make_float4(0.25f * lo[4], 0.25f * lo[5], 0.25f * lo[6], 0.25f * lo[7]);
-    o[2] = make_float4(0.25f * hi[0], 0.25f * hi[1], 0.25f * hi[2], 0.25f * hi[3]);
-    o[3] = make_float4(0.25f * hi[4], 0.25f * hi[5], 0.25f * hi[6], 0.25f * hi[7]);
+  const uint32_t lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  constexpr int64_t kPerWave = 64 * kQuarters;
+  float4* __restrict__ o = reinterpret_cast<float4*>(y);
+  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
+    float z[kQuarters][4];
+    if (base + kPerWave <= nq) {           // wave-uniform: every quarter in range
+#pragma unroll
+      for (int j = 0; j < kQuarters; ++j) load_quarter(x, base + j * 64 + lane, z[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kQuarters; ++j) {
+        const int64_t pc = base + j * 64 + lane;
+        if (pc < nq) {
+          load_quarter(x, pc, z[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[j][i] = 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kQuarters; ++j) {
+      stages_1_2(z[j]);
+      quad_stages_4_8(z[j], lane);
+      const int64_t pc = base + j * 64 + lane;
+      if (pc < nq)
+        o[pc] = make_float4(0.25f * z[j][0], 0.25f * z[j][1], 0.25f * z[j][2], 0.25f * z[j][3]);
+    }
   }
 }
 
@@ -414,39 +455,42 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const T* __restrict_
 }
 
 // MXFP4 dequantize: +-GRID[c & 7] * 2^(byte - 127), rounded to binary32, then
-// the inverse rotation of each half (the same butterfly and * 0.25).
+// the inverse rotation of each 16-element half (the same butterfly and
+// * 0.25).  Quarter-block layout as for the NVFP4 decode; a 32-element block
+// is two quads.
 __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ q,
                                                               const uint8_t* __restrict__ s,
-                                                              int64_t nb32, int rotate,
+                                                              int64_t nq, int rotate,
                                                               float* __restrict__ y) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb32; b += stride) {
-    const uint4 w = *reinterpret_cast<const uint4*>(q + b * 16);
-    const float sc = ldexpf(1.0f, static_cast<int>(s[b]) - 127);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float v[4][8];
+  const uint32_t lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  constexpr int64_t kPerWave = 64 * kQuarters;
+  const uint16_t* __restrict__ q2 = reinterpret_cast<const uint16_t*>(q);
+  float4* __restrict__ o = reinterpret_cast<float4*>(y);
+  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
+    uint32_t c[kQuarters], sb[kQuarters];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[k][i] = e2m1_value((ww[k] >> (4 * i)) & 15u) * sc;
-    if (rotate) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        stages_1_2_4(v[2 * h]);
-        stages_1_2_4(v[2 * h + 1]);
-        stage_8(v[2 * h], v[2 * h + 1]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          v[2 * h][i] = 0.25f * v[2 * h][i];
-          v[2 * h + 1][i] = 0.25f * v[2 * h + 1][i];
-        }
-      }
+    for (int j = 0; j < kQuarters; ++j) {
+      const int64_t pc = base + j * 64 + lane;
+      const bool in = pc < nq;
+      c[j] = in ? q2[pc] : 0u;
+      sb[j] = in ? s[pc >> 3] : 127u;
     }
-    float4* o = reinterpret_cast<float4*>(y + b * 32);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      o[2 * k] = make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
-      o[2 * k + 1] = make_float4(v[k][4], v[k][5], v[k][6], v[k][7]);
+    for (int j = 0; j < kQuarters; ++j) {
+      const float sc = ldexpf(1.0f, static_cast<int>(sb[j]) - 127);
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = e2m1_value((c[j] >> (4 * i)) & 15u) * sc;
+      if (rotate) {
+        stages_1_2(z);
+        quad_stages_4_8(z, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = 0.25f * z[i];
+      }
+      const int64_t pc = base + j * 64 + lane;
+      if (pc < nq) o[pc] = make_float4(z[0], z[1], z[2], z[3]);
     }
   }
 }
@@ -516,6 +560,13 @@ int quant_grid(int64_t nb) {
 }
 
 int generic_grid(int64_t nb) { return clamp_grid(8LL * device_cus(), (nb + kThreads - 1) / kThreads); }
+
+// Quarter-block kernels: 8 workgroups per compute unit, kThreads * kQuarters
+// quarters per workgroup iteration.
+int quarter_grid(int64_t nq) {
+  const int64_t per_wg = static_cast<int64_t>(kThreads) * kQuarters;
+  return clamp_grid(8LL * device_cus(), (nq + per_wg - 1) / per_wg);
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -671,7 +722,8 @@ nvfp4_status rotate_only(const T* x, int64_t rows, int64_t cols, float* y, hipSt
   if (overlap(range_of(x, n * static_cast<int64_t>(sizeof(T))), range_of(y, n * 4)))
     return NVFP4_ERR_ARG;
   if (nb == 0) return NVFP4_OK;
-  return launch(rotate_kernel<T>, dim3(generic_grid(nb)), dim3(kThreads), st, x, nb, y) == hipSuccess
+  const int64_t nq = 4 * nb;
+  return launch(rotate_kernel<T>, dim3(quarter_grid(nq)), dim3(kThreads), st, x, nq, y) == hipSuccess
              ? NVFP4_OK
              : NVFP4_ERR_HIP;
 }
@@ -730,7 +782,8 @@ nvfp4_status nvfp4_dequant(const uint8_t* q, const uint8_t* s, const float* gsca
       overlap(ry, range_of(gscale, 4)))
     return NVFP4_ERR_ARG;
   if (nb == 0) return NVFP4_OK;
-  if (launch(dequant_kernel, dim3(generic_grid(nb)), dim3(kThreads), stream, q, s, gscale, nb, rotate,
+  const int64_t nq = 4 * nb;
+  if (launch(dequant_kernel, dim3(quarter_grid(nq)), dim3(kThreads), stream, q, s, gscale, nq, rotate,
              y_out) != hipSuccess)
     return NVFP4_ERR_HIP;
   return NVFP4_OK;
@@ -770,7 +823,8 @@ nvfp4_status mxfp4_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int
   if (overlap(ry, range_of(q, n / 2)) || overlap(ry, range_of(s, n / 32))) return NVFP4_ERR_ARG;
   const int64_t nb32 = n / 32;
   if (nb32 == 0) return NVFP4_OK;
-  if (launch(mx_dequant_kernel, dim3(generic_grid(nb32)), dim3(kThreads), stream, q, s, nb32, rotate,
+  const int64_t nq = 8 * nb32;
+  if (launch(mx_dequant_kernel, dim3(quarter_grid(nq)), dim3(kThreads), stream, q, s, nq, rotate,
              y_out) != hipSuccess)
     return NVFP4_ERR_HIP;
   return NVFP4_OK;

@@ -88,6 +88,25 @@ __device__ __forceinline__ float swap_lane1(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
+// Lane exchange within a quad: quad_perm [2,3,0,1] (lane ^ 2).
+__device__ __forceinline__ float swap_lane2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// Strides 4 and 8 for a block spread over the four lanes of a quad, lane t of
+// the quad holding elements 4t..4t+3 (strides 1 and 2 already applied in
+// lane).  Stride 4 pairs lanes t and t^1, stride 8 lanes t and t^2.  The lane
+// that holds the pair's first element a keeps a + b; its partner, holding b,
+// forms a - b as a + (-b), which is the same binary32 operation.  Every lane
+// of the quad must execute this (the exchange reads the partner's register).
+__device__ __forceinline__ void quad_stages_4_8(float z[4], uint32_t lane) {
+  const uint32_t s1 = (lane & 1u) << 31, s2 = (lane & 2u) << 30;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = swap_lane1(z[i]) + __uint_as_float(__float_as_uint(z[i]) ^ s1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = swap_lane2(z[i]) + __uint_as_float(__float_as_uint(z[i]) ^ s2);
+}
+
 // ---------------------------------------------------------------- division
 
 // RN(1/6) as a binary32.

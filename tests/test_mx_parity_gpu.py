@@ -186,3 +186,16 @@ def test_dequant_round_trip(nv, name, rotate):
     err = np.abs(y.cpu().numpy().astype(np.float64) - yd)
     # fp32 decode: each output is a 16-term signed sum, rounded per step
     assert np.all(err <= 1e-6 * np.abs(yd).reshape(-1, 16).max(1).repeat(16).reshape(yd.shape))
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("rotate", [True, False])
+def test_dequant_small_shapes(nv, rows, cols, rotate):
+    x = mixed_input(rows, cols, "f32", seed=rows * 17 + cols)
+    q, s = nv.mx_rotquant(to_dev(x), rotate=rotate)
+    y = nv.mx_dequant(q, s, rotate=rotate)
+    torch.cuda.synchronize()
+    compare(f"{rows}x{cols} rotate={rotate}", x, rotate, (q, s))
+    yd = oracle.mx_dequant_f64(q.cpu().numpy(), s.cpu().numpy(), rotate)
+    tol = 1e-6 * np.abs(yd).reshape(-1, 16).max(1).repeat(16).reshape(yd.shape)
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - yd) <= tol)

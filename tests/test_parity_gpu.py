@@ -371,3 +371,18 @@ def test_dequant_round_trip(nv, name, rotate):
     yd = oracle.dequant_f64(oq, os_, og, rotate)
     scale = np.abs(yd).max()
     assert np.max(np.abs(y.cpu().numpy().astype(np.float64) - yd)) <= 1e-6 * scale
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("rotate", [True, False])
+def test_dequant_small_shapes(nv, rows, cols, rotate):
+    """Decode on shapes whose quarter-block count leaves a ragged last
+    iteration, element by element against the oracle's fp64 decode."""
+    x = mixed_input(rows, cols, "bf16", seed=rows * 13 + cols)
+    q, s, g, a = nv.rotquant(to_dev(x), rotate=rotate)
+    y = nv.dequant(q, s, g, rotate=rotate)
+    torch.cuda.synchronize()
+    compare(f"{rows}x{cols} rotate={rotate}", x, rotate, (q, s, g, a))
+    yd = oracle.dequant_f64(q.cpu().numpy(), s.cpu().numpy(), float(g.cpu()[0]), rotate)
+    tol = 1e-6 * np.abs(yd).reshape(-1, 16).max(1).repeat(16).reshape(yd.shape)
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - yd) <= tol)

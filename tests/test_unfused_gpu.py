@@ -36,7 +36,7 @@ def to_dev(x: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(x).to("cuda:0")
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (300, 4112), (257, 8192)])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (127, 16), (300, 4112), (257, 8192), (1000, 1040)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rotate16_matches_oracle(nv, rows, cols, dtype):
     n = rows * cols

@@ -264,6 +264,11 @@ def main() -> int:
     unfused_bytes = 2 * n + 4 * n + 4 * n + 4 * n + n // 2 + n // 16 + 8
     unfused_same = bool(torch.equal(qu, q) and torch.equal(su, s) and torch.equal(gu, g))
 
+    # Context: the same step writing the block scales in the 128 x 4-tile
+    # swizzled layout (same bytes moved; only the scale-store addresses differ).
+    sw = torch.empty(nv.swizzled_scale_bytes(ROWS, COLS), dtype=torch.uint8, device=dev)
+    sw_ms = timed(lambda: nv.rotquant_swizzled(x, rotate=True, out=(qu, sw, gu, au)))
+
     # Context: decode (codes + scales + g in, fp32 out, inverse rotation).
     yd = nv.dequant(q, s, g, rotate=True)
     dq_ms = timed(lambda: nv.dequant(q, s, g, rotate=True, out=yd))
@@ -316,6 +321,8 @@ def main() -> int:
                                  "gbs": round(unfused_bytes / (unfused_ms * 1e-3) / 1e9, 2),
                                  "fused_speedup": round(unfused_ms / ms, 3),
                                  "same_bytes_as_fused": unfused_same},
+        "swizzled_scales_step": {"ms": round(sw_ms, 5),
+                                 "gbs": round(nbytes["step"] / (sw_ms * 1e-3) / 1e9, 2)},
         "dequant": {"ms": round(dq_ms, 5), "bytes_per_elem": round(dq_bytes / n, 4),
                     "gbs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 2)},
         "timed_wall_s": round(wall, 4),

@@ -145,6 +145,35 @@ nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gsca
                            hipStream_t stream);
 
 /*
+ * Block scales in the swizzled tiled layout (page "A Fused Hadamard + NVFP4
+ * Quantization Kernel in Triton", section 6: GEMMs read scales tiled, and a
+ * production kernel writes that layout itself).  The page does not give the
+ * layout; the one used is the tiled layout of the GEMM library documentation
+ * it cites for 16-element block scales: the [rows, cols/16] scale matrix S,
+ * padded with zero bytes to multiples of 128 rows and 4 columns, cut into
+ * 128 x 4 tiles of 512 bytes stored tile-row by tile-row, with
+ * S[128*rt + 32*i + j][4*ct + k] (i, k < 4, j < 32) at byte
+ * 512*(rt*ceil(cols/64) + ct) + 16*j + 4*i + k.
+ *
+ * nvfp4_swizzled_scale_bytes: size of that buffer, 512*ceil(rows/128)*
+ * ceil(cols/64); -1 for a bad shape or more than 2^32 - 1 blocks.
+ * nvfp4_rotquant_swizzled(_f32): nvfp4_rotquant with s_out in this layout
+ * (s_out holds nvfp4_swizzled_scale_bytes bytes, 4-byte aligned; padding bytes
+ * are written as 0).  Codes, g and amax are as for nvfp4_rotquant.
+ * nvfp4_dequant_swizzled: nvfp4_dequant reading scales in this layout.
+ */
+int64_t nvfp4_swizzled_scale_bytes(int64_t rows, int64_t cols);
+nvfp4_status nvfp4_rotquant_swizzled(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,
+                                     uint8_t *q_out, uint8_t *s_out, float *gscale_out,
+                                     float *amax_out, hipStream_t stream);
+nvfp4_status nvfp4_rotquant_swizzled_f32(const float *x, int64_t rows, int64_t cols, int rotate,
+                                         uint8_t *q_out, uint8_t *s_out, float *gscale_out,
+                                         float *amax_out, hipStream_t stream);
+nvfp4_status nvfp4_dequant_swizzled(const uint8_t *q, const uint8_t *s, const float *gscale,
+                                    int64_t rows, int64_t cols, int rotate, float *y_out,
+                                    hipStream_t stream);
+
+/*
  * Rotation alone: y = x H16 on every 16-element block (butterfly with strides
  * 1, 2, 4, 8, then * 0.25; the arithmetic of nvfp4_rotquant's rotation), stored
  * as fp32 [rows, cols].  With nvfp4_rotamax_f32 and nvfp4_quant_from_amax_f32

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "LIB_PATH", "Nvfp4Error", "rotquant", "rotamax", "quant_from_amax", "dequant",
     "status_string", "lib", "mx_rotquant", "mx_dequant",
-    "rotate16",
+    "rotate16", "rotquant_swizzled", "dequant_swizzled", "swizzled_scale_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +46,9 @@ _SIGS = {
     "nvfp4_quant_from_amax_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_dequant": [_p, _p, _p, _i64, _i64, _int, _p, _p],
     "nvfp4_rotate16": [_p, _i64, _i64, _p, _p],
+    "nvfp4_rotquant_swizzled": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
+    "nvfp4_rotquant_swizzled_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
+    "nvfp4_dequant_swizzled": [_p, _p, _p, _i64, _i64, _int, _p, _p],
     "nvfp4_rotate16_f32": [_p, _i64, _i64, _p, _p],
     "mxfp4_rotquant": [_p, _i64, _i64, _int, _p, _p, _p],
     "mxfp4_rotquant_f32": [_p, _i64, _i64, _int, _p, _p, _p],
@@ -55,6 +58,8 @@ for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = _int
+lib.nvfp4_swizzled_scale_bytes.argtypes = [_i64, _i64]
+lib.nvfp4_swizzled_scale_bytes.restype = _i64
 lib.nvfp4_status_string.argtypes = [_int]
 lib.nvfp4_status_string.restype = ctypes.c_char_p
 
@@ -165,6 +170,41 @@ def dequant(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = Tr
     _check("nvfp4_dequant", lib.nvfp4_dequant(_ptr(q), _ptr(s), _ptr(g), rows, cols,
                                               int(bool(rotate)), _ptr(out),
                                               _stream(q.device, stream)))
+    return out
+
+
+def swizzled_scale_bytes(rows: int, cols: int) -> int:
+    n = int(lib.nvfp4_swizzled_scale_bytes(rows, cols))
+    if n < 0:
+        raise ValueError(f"no swizzled scale layout for shape ({rows}, {cols})")
+    return n
+
+
+def rotquant_swizzled(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, stream=None):
+    """rotquant with the block scales in the 128 x 4-tile swizzled layout.
+    Returns (q uint8 [rows, cols/2], s uint8 [swizzled_scale_bytes], g, amax)."""
+    rows, cols = _check_input(x)
+    if out is None:
+        q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+        s = torch.empty(swizzled_scale_bytes(rows, cols), dtype=torch.uint8, device=x.device)
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+        a = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        q, s, g, a = out
+    fn = _variant(x, "nvfp4_rotquant_swizzled")
+    _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(q), _ptr(s),
+                                _ptr(g), _ptr(a), _stream(x.device, stream)))
+    return q, s, g, a
+
+
+def dequant_swizzled(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = True,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    rows, cols = q.shape[0], q.shape[1] * 2
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.float32, device=q.device)
+    _check("nvfp4_dequant_swizzled", lib.nvfp4_dequant_swizzled(
+        _ptr(q), _ptr(s), _ptr(g), rows, cols, int(bool(rotate)), _ptr(out),
+        _stream(q.device, stream)))
     return out
 
 

@@ -180,6 +180,43 @@ __global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __re
   workgroup_max_to(m, amax_bits);
 }
 
+// Where block b's scale byte is stored.  Row-major: byte b of the
+// [rows, cols/16] matrix.  Swizzled (the tiled layout GEMMs read, page "A
+// Fused Hadamard + NVFP4 Quantization Kernel in Triton", section 6; layout as
+// the GEMM library documentation it cites defines it for 16-element block
+// scales): the matrix padded to 128-row x 4-column tiles of 512 bytes, tiles
+// stored tile-row by tile-row, and S[128 rt + 32 i + j][4 ct + k] at byte
+// 512 (rt * ctiles + ct) + 16 j + 4 i + k.  Block indices fit in 32 bits
+// (checked on the host).
+struct RowMajorScales {
+  __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
+};
+struct SwizzledScales {
+  uint32_t cb, ctiles;  // blocks per row, ceil(cb / 4)
+  __device__ __forceinline__ int64_t operator()(int64_t b) const {
+    const uint32_t bb = static_cast<uint32_t>(b);
+    const uint32_t r = bb / cb, c = bb - r * cb;
+    const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
+    return static_cast<int64_t>(tile * 512u + (((r & 31u) << 4) | (((r >> 5) & 3u) << 2) | (c & 3u)));
+  }
+};
+
+// Zero the bytes of a swizzled scale buffer that belong to no block (rows
+// past the last one, columns past cb): launched only when such padding exists.
+__global__ __launch_bounds__(kThreads) void swizzle_pad_kernel(uint8_t* __restrict__ s, int64_t rows,
+                                                               uint32_t cb, uint32_t ctiles,
+                                                               int64_t total) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total; i += stride) {
+    const int64_t tile = i >> 9;
+    const uint32_t inner = static_cast<uint32_t>(i & 511);
+    const int64_t rt = tile / ctiles, ct = tile - rt * ctiles;
+    const int64_t r = rt * 128 + ((inner >> 2) & 3u) * 32 + (inner >> 4);
+    const int64_t c = ct * 4 + (inner & 3u);
+    if (r >= rows || c >= cb) s[i] = 0;
+  }
+}
+
 // Pass 2 body: each lane rotates, scales and encodes one block per iteration.
 // Workgroup w handles the 256-block chunks w, w + G, w + 2G, ... (G = grid
 // size), last chunk first: the chunks pass 1 read last are the likeliest to
@@ -194,10 +231,11 @@ __global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __re
 // 4 are exact there), the divisions are corrected reciprocal products and the
 // per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
 // Otherwise every division is a true binary32 division.
-template <typename T, bool ROTATE, bool FAST>
+template <typename T, bool ROTATE, bool FAST, typename SMAP>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
                                              const float2* __restrict__ tab,
-                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                             SMAP smap) {
   const int64_t nchunks = (nb + kThreads - 1) / kThreads;
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
@@ -259,17 +297,18 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
       }
     }
     *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
-    s[b] = static_cast<uint8_t>(sb);
+    s[smap(b)] = static_cast<uint8_t>(sb);
   }
 }
 
-template <typename T, bool ROTATE>
+template <typename T, bool ROTATE, typename SMAP>
 __global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
                                                             const uint32_t* __restrict__ amax_bits,
                                                             int allow_fast,
                                                             uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ s,
-                                                            float* __restrict__ gscale_out) {
+                                                            float* __restrict__ gscale_out,
+                                                            SMAP smap) {
   __shared__ float2 tab[128];
   const uint32_t abits = *amax_bits;
   const float g = global_scale(__uint_as_float(abits));
@@ -283,11 +322,11 @@ __global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict_
         tab[threadIdx.x] = make_float2(d, 1.0f / d);
       }
       __syncthreads();
-      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s);
+      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap);
       return;
     }
   }
-  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s);
+  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap);
 }
 
 // Kernels that write fp32 per element (decode, rotation alone) use a
@@ -314,11 +353,12 @@ __device__ __forceinline__ void load_quarter(const uint16_t* __restrict__ x, int
 // Dequantize (section 2, dequantize): +-GRID[c & 7] * RN(float(s) * g), then
 // the same butterfly and * 0.25 when rotated (H16 is symmetric, so H16^T is
 // the forward transform).  nq = number of quarters = rows * cols / 4.
+template <typename SMAP>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ s,
                                                            const float* __restrict__ gscale,
                                                            int64_t nq, int rotate,
-                                                           float* __restrict__ y) {
+                                                           float* __restrict__ y, SMAP smap) {
   const uint32_t lane = threadIdx.x & 63;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
@@ -333,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
       const int64_t pc = base + j * 64 + lane;
       const bool in = pc < nq;
       c[j] = in ? q2[pc] : 0u;
-      sb[j] = in ? s[pc >> 2] : 0u;
+      sb[j] = in ? s[smap(pc >> 2)] : 0u;
     }
 #pragma unroll
     for (int j = 0; j < kQuarters; ++j) {
@@ -591,7 +631,7 @@ nvfp4_status check_shape(int64_t rows, int64_t cols, int64_t* nb) {
 template <typename T>
 nvfp4_status validate_quant(const T* x, int64_t rows, int64_t cols, int rotate, const uint8_t* q,
                             const uint8_t* s, const float* g, const float* amax, int64_t* nb,
-                            bool amax_is_input) {
+                            bool amax_is_input, int64_t s_bytes = -1) {
   nvfp4_status st = check_shape(rows, cols, nb);
   if (st != NVFP4_OK) return st;
   const int64_t n = rows * cols;
@@ -600,7 +640,7 @@ nvfp4_status validate_quant(const T* x, int64_t rows, int64_t cols, int rotate, 
   if (n != 0 && (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4))) return NVFP4_ERR_ALIGN;
   if (!aligned(g, 4) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
   const Range rx = range_of(x, n * static_cast<int64_t>(sizeof(T)));
-  const Range rq = range_of(q, n / 2), rs = range_of(s, n / 16);
+  const Range rq = range_of(q, n / 2), rs = range_of(s, s_bytes < 0 ? n / 16 : s_bytes);
   const Range rg = range_of(g, 4), ra = range_of(amax, 4);
   const Range outs[4] = {rq, rs, rg, ra};
   const int n_out = amax_is_input ? 3 : 4;
@@ -639,16 +679,46 @@ nvfp4_status enqueue_rotamax(const T* x, int64_t nb, int rotate, float* amax, hi
   return launch_rotamax(x, nb, rotate, bits, st) == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-template <typename T>
+template <typename T, typename SMAP = RowMajorScales>
 nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const float* amax, uint8_t* q,
-                           uint8_t* s, float* g, hipStream_t st) {
+                           uint8_t* s, float* g, hipStream_t st, SMAP smap = SMAP{}) {
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(amax);
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
   const dim3 grid(quant_grid(nb));
   const hipError_t e =
-      rotate ? launch(rotquant_kernel<T, true>, grid, dim3(kThreads), st, x, nb, bits, allow_fast, q, s, g)
-             : launch(rotquant_kernel<T, false>, grid, dim3(kThreads), st, x, nb, bits, allow_fast, q, s, g);
+      rotate ? launch(rotquant_kernel<T, true, SMAP>, grid, dim3(kThreads), st, x, nb, bits, allow_fast,
+                      q, s, g, smap)
+             : launch(rotquant_kernel<T, false, SMAP>, grid, dim3(kThreads), st, x, nb, bits,
+                      allow_fast, q, s, g, smap);
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+// Size of the swizzled scale buffer for a [rows, cols] tensor; -1 for a bad
+// shape or more than 2^32 - 1 blocks.
+int64_t swizzled_bytes(int64_t rows, int64_t cols) {
+  int64_t nb = 0;
+  if (check_shape(rows, cols, &nb) != NVFP4_OK || nb > 0xFFFFFFFFLL) return -1;
+  const int64_t cb = cols / 16;
+  return ((rows + 127) / 128) * ((cb + 3) / 4) * 512;
+}
+
+template <typename T>
+nvfp4_status rotquant_swizzled(const T* x, int64_t rows, int64_t cols, int rotate, uint8_t* q,
+                               uint8_t* s, float* g, float* amax, hipStream_t st) {
+  const int64_t sbytes = swizzled_bytes(rows, cols);
+  if (sbytes < 0) return NVFP4_ERR_SHAPE;
+  int64_t nb = 0;
+  nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, false, sbytes);
+  if (r != NVFP4_OK) return r;
+  const uint32_t cb = static_cast<uint32_t>(cols / 16), ctiles = (cb + 3) / 4;
+  if (nb != 0 && (rows % 128 != 0 || cb % 4 != 0)) {
+    if (launch(swizzle_pad_kernel, dim3(generic_grid(sbytes)), dim3(kThreads), st, s, rows, cb, ctiles,
+               sbytes) != hipSuccess)
+      return NVFP4_ERR_HIP;
+  }
+  r = enqueue_rotamax(x, nb, rotate, amax, st);
+  if (r != NVFP4_OK) return r;
+  return enqueue_quant(x, nb, rotate, amax, q, s, g, st, SwizzledScales{cb, ctiles});
 }
 
 template <typename T>
@@ -727,6 +797,30 @@ nvfp4_status rotate_only(const T* x, int64_t rows, int64_t cols, float* y, hipSt
              ? NVFP4_OK
              : NVFP4_ERR_HIP;
 }
+template <typename SMAP>
+nvfp4_status dequant(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t rows,
+                     int64_t cols, int rotate, float* y_out, hipStream_t stream, int64_t s_bytes,
+                     SMAP smap) {
+  int64_t nb = 0;
+  nvfp4_status r = check_shape(rows, cols, &nb);
+  if (r != NVFP4_OK) return r;
+  const int64_t n = rows * cols;
+  if ((n != 0 && (!q || !s || !y_out)) || !gscale) return NVFP4_ERR_NULL;
+  if (rotate != 0 && rotate != 1) return NVFP4_ERR_ARG;
+  if ((n != 0 && (!aligned(q, 8) || !aligned(y_out, 16))) || !aligned(gscale, 4))
+    return NVFP4_ERR_ALIGN;
+  const Range ry = range_of(y_out, n * 4);
+  if (overlap(ry, range_of(q, n / 2)) || overlap(ry, range_of(s, s_bytes < 0 ? n / 16 : s_bytes)) ||
+      overlap(ry, range_of(gscale, 4)))
+    return NVFP4_ERR_ARG;
+  if (nb == 0) return NVFP4_OK;
+  const int64_t nq = 4 * nb;
+  if (launch(dequant_kernel<SMAP>, dim3(quarter_grid(nq)), dim3(kThreads), stream, q, s, gscale, nq,
+             rotate, y_out, smap) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -769,24 +863,31 @@ nvfp4_status nvfp4_quant_from_amax_f32(const float* x, int64_t rows, int64_t col
 
 nvfp4_status nvfp4_dequant(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t rows,
                            int64_t cols, int rotate, float* y_out, hipStream_t stream) {
-  int64_t nb = 0;
-  nvfp4_status r = check_shape(rows, cols, &nb);
-  if (r != NVFP4_OK) return r;
-  const int64_t n = rows * cols;
-  if ((n != 0 && (!q || !s || !y_out)) || !gscale) return NVFP4_ERR_NULL;
-  if (rotate != 0 && rotate != 1) return NVFP4_ERR_ARG;
-  if ((n != 0 && (!aligned(q, 8) || !aligned(y_out, 16))) || !aligned(gscale, 4))
-    return NVFP4_ERR_ALIGN;
-  const Range ry = range_of(y_out, n * 4);
-  if (overlap(ry, range_of(q, n / 2)) || overlap(ry, range_of(s, n / 16)) ||
-      overlap(ry, range_of(gscale, 4)))
-    return NVFP4_ERR_ARG;
-  if (nb == 0) return NVFP4_OK;
-  const int64_t nq = 4 * nb;
-  if (launch(dequant_kernel, dim3(quarter_grid(nq)), dim3(kThreads), stream, q, s, gscale, nq, rotate,
-             y_out) != hipSuccess)
-    return NVFP4_ERR_HIP;
-  return NVFP4_OK;
+  return dequant(q, s, gscale, rows, cols, rotate, y_out, stream, -1, RowMajorScales{});
+}
+
+int64_t nvfp4_swizzled_scale_bytes(int64_t rows, int64_t cols) { return swizzled_bytes(rows, cols); }
+
+nvfp4_status nvfp4_rotquant_swizzled(const uint16_t* x_bf16, int64_t rows, int64_t cols, int rotate,
+                                     uint8_t* q_out, uint8_t* s_out, float* gscale_out,
+                                     float* amax_out, hipStream_t stream) {
+  return rotquant_swizzled(x_bf16, rows, cols, rotate, q_out, s_out, gscale_out, amax_out, stream);
+}
+
+nvfp4_status nvfp4_rotquant_swizzled_f32(const float* x, int64_t rows, int64_t cols, int rotate,
+                                         uint8_t* q_out, uint8_t* s_out, float* gscale_out,
+                                         float* amax_out, hipStream_t stream) {
+  return rotquant_swizzled(x, rows, cols, rotate, q_out, s_out, gscale_out, amax_out, stream);
+}
+
+nvfp4_status nvfp4_dequant_swizzled(const uint8_t* q, const uint8_t* s, const float* gscale,
+                                    int64_t rows, int64_t cols, int rotate, float* y_out,
+                                    hipStream_t stream) {
+  const int64_t sbytes = swizzled_bytes(rows, cols);
+  if (sbytes < 0) return NVFP4_ERR_SHAPE;
+  const uint32_t cb = static_cast<uint32_t>(cols / 16);
+  return dequant(q, s, gscale, rows, cols, rotate, y_out, stream, sbytes,
+                 SwizzledScales{cb, (cb + 3) / 4});
 }
 
 nvfp4_status nvfp4_rotate16(const uint16_t* x_bf16, int64_t rows, int64_t cols, float* y_out,

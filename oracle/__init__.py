@@ -70,6 +70,9 @@ def _load():
     lib.oracle_mx_quantize.restype = _int
     lib.oracle_mx_roundtrip_error.argtypes = [_ptr, _int, _i64, _i64, _int, _ptr, _ptr, _int]
     lib.oracle_mx_roundtrip_error.restype = ctypes.c_double
+    lib.oracle_swizzled_scale_bytes.argtypes = [_i64, _i64]
+    lib.oracle_swizzled_scale_bytes.restype = _i64
+    lib.oracle_swizzle_scales.argtypes = [_ptr, _i64, _i64, _ptr]
     lib.oracle_rotate_tensor.argtypes = [_ptr, _int, _i64, _i64, _ptr, _int]
     lib.oracle_rotate_tensor.restype = _int
     lib.oracle_mx_dequant_f64.argtypes = [_ptr, _ptr, _i64, _i64, _int, _ptr, _int]
@@ -248,4 +251,20 @@ def mx_dequant_f64(q: np.ndarray, s: np.ndarray, rotate: bool, nthreads: int = 0
     out = np.empty((rows, cols), dtype=np.float64)
     _load().oracle_mx_dequant_f64(_p(np.ascontiguousarray(q)), _p(np.ascontiguousarray(s)),
                                   rows, cols, int(rotate), _p(out), nthreads)
+    return out
+
+
+# ---------------------------------------------------------------- swizzled scales
+
+def swizzled_scale_bytes(rows: int, cb: int) -> int:
+    return int(_load().oracle_swizzled_scale_bytes(rows, cb))
+
+
+def swizzle_scales(s: np.ndarray) -> np.ndarray:
+    """Row-major block scales [rows, cols/16] -> the padded 128 x 4-tile layout
+    (1-D uint8, zero padding)."""
+    ss = np.ascontiguousarray(s, dtype=np.uint8)
+    rows, cb = ss.shape
+    out = np.empty(swizzled_scale_bytes(rows, cb), dtype=np.uint8)
+    _load().oracle_swizzle_scales(_p(ss), rows, cb, _p(out))
     return out

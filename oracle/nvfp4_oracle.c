@@ -659,3 +659,41 @@ int oracle_rotate_tensor(const void *x, int is_f32, int64_t rows, int64_t cols, 
     (void)nthreads;
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Swizzled block-scale layout                                        */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The page "A Fused Hadamard + NVFP4 Quantization Kernel in Triton", section 6
+ * ("Layout"), says NVFP4 GEMMs read block scales in a swizzled tiled layout
+ * rather than the row-major [rows, cols/16] matrix, and that a production
+ * kernel writes that layout directly; it does not spell the layout out.
+ * Reading taken: the tiled layout of the GEMM library documentation the page
+ * cites for 16-element block scales.  The scale matrix S [rows, cb] (cb =
+ * cols / 16) is padded with zero bytes to multiples of 128 rows and 4
+ * columns and cut into 128 x 4 tiles of 512 bytes, stored tile-row by
+ * tile-row (tile (rt, ct) at byte (rt * ceil(cb / 4) + ct) * 512).  Inside a
+ * tile, S[rt*128 + 32*i + j][ct*4 + k] (i, k < 4, j < 32) sits at byte
+ * 16*j + 4*i + k: each 16-byte line holds rows j, j+32, j+64, j+96.
+ */
+int64_t oracle_swizzled_scale_bytes(int64_t rows, int64_t cb)
+{
+    int64_t rt = (rows + 127) / 128, ct = (cb + 3) / 4;
+    return rt * ct * 512;
+}
+
+void oracle_swizzle_scales(const uint8_t *s, int64_t rows, int64_t cb, uint8_t *out)
+{
+    int64_t ctiles = (cb + 3) / 4;
+    int64_t total = oracle_swizzled_scale_bytes(rows, cb);
+    for (int64_t i = 0; i < total; i++)
+        out[i] = 0;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t c = 0; c < cb; c++) {
+            int64_t tile = (r / 128) * ctiles + c / 4;
+            int64_t inner = 16 * (r % 32) + 4 * ((r % 128) / 32) + (c % 4);
+            out[tile * 512 + inner] = s[r * cb + c];
+        }
+    }
+}

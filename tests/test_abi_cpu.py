@@ -38,6 +38,11 @@ def lib():
     lib.mxfp4_dequant.argtypes = [p, p, i64, i64, i, p, p]
     for name in ("nvfp4_rotate16", "nvfp4_rotate16_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, p, p]
+    for name in ("nvfp4_rotquant_swizzled", "nvfp4_rotquant_swizzled_f32"):
+        getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p]
+    lib.nvfp4_dequant_swizzled.argtypes = [p, p, p, i64, i64, i, p, p]
+    lib.nvfp4_swizzled_scale_bytes.argtypes = [i64, i64]
+    lib.nvfp4_swizzled_scale_bytes.restype = i64
     lib.nvfp4_status_string.argtypes = [i]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     return lib
@@ -48,7 +53,9 @@ def test_header_declares_the_boundary():
     for must in ("nvfp4_rotquant", "nvfp4_rotquant_f32", "nvfp4_dequant",
                  "nvfp4_status_string", "nvfp4_rotamax", "nvfp4_quant_from_amax",
                  "mxfp4_rotquant", "mxfp4_rotquant_f32", "mxfp4_dequant",
-                 "nvfp4_rotate16", "nvfp4_rotate16_f32"):
+                 "nvfp4_rotate16", "nvfp4_rotate16_f32", "nvfp4_rotquant_swizzled",
+                 "nvfp4_rotquant_swizzled_f32", "nvfp4_dequant_swizzled",
+                 "nvfp4_swizzled_scale_bytes"):
         assert must in names
 
 
@@ -177,3 +184,39 @@ def test_rotate_validation(lib, name):
     assert f(X, 4, 64, Y + 4, None) == ERR_ALIGN
     assert f(X, 4, 64, X + 64, None) == ERR_ARG
     assert f(None, 0, 64, None, None) == OK
+
+
+def test_swizzled_scale_bytes(lib):
+    f = lib.nvfp4_swizzled_scale_bytes
+    assert f(128, 64) == 512
+    assert f(129, 64) == 1024
+    assert f(128, 80) == 1024
+    assert f(16384, 8192) == 16384 * 512
+    assert f(0, 64) == 0
+    assert f(1, 16) == 512
+    assert f(4, 40) == -1
+    assert f(-1, 64) == -1
+    assert f(1 << 20, 1 << 20) == -1          # more than 2^32 - 1 blocks
+
+
+@pytest.mark.parametrize("name", ["nvfp4_rotquant_swizzled", "nvfp4_rotquant_swizzled_f32"])
+def test_swizzled_quant_validation(lib, name):
+    f = lambda **kw: rq(lib, name=name, **kw)  # noqa: E731
+    assert f(x=None) == ERR_NULL
+    assert f(s=None) == ERR_NULL
+    assert f(cols=24) == ERR_SHAPE
+    assert f(rotate=2) == ERR_ARG
+    assert f(q=Q + 8) == ERR_ALIGN
+    assert f(s=S + 2) == ERR_ALIGN
+    assert f(s=X + 64) == ERR_ARG            # inside the input
+    assert f(q=S - 64) == ERR_ARG            # codes run into the 512-byte scale tile
+    assert f(rows=1 << 20, cols=1 << 20) == ERR_SHAPE
+
+
+def test_swizzled_dequant_validation(lib):
+    f = lib.nvfp4_dequant_swizzled
+    Y = 0x80000
+    assert f(None, S, G, 4, 64, 1, Y, None) == ERR_NULL
+    assert f(Q, S, G, 4, 40, 1, Y, None) == ERR_SHAPE
+    assert f(Q, S, G, 4, 64, 3, Y, None) == ERR_ARG
+    assert f(Q, S, G, 4, 64, 1, S - 64, None) == ERR_ARG

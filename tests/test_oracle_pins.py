@@ -592,3 +592,40 @@ def test_quantizing_the_stored_rotation_equals_the_fused_definition():
         b = oracle.quantize(y, False)
         for u, v in zip(a, b):
             assert np.array_equal(np.asarray(u), np.asarray(v)), name
+
+
+# ---------------------------------------------------------------- swizzled scales
+
+def _swizzle_by_reshape(s: np.ndarray) -> np.ndarray:
+    """The tiled layout as a tensor reshape: pad to [128 RT, 4 CT], view as
+    [RT, 4 (i), 32 (j), CT, 4 (k)] with row = 128 rt + 32 i + j, then order the
+    axes (rt, ct, j, i, k)."""
+    rows, cb = s.shape
+    rt, ct = -(-rows // 128), -(-cb // 4)
+    pad = np.zeros((rt * 128, ct * 4), dtype=np.uint8)
+    pad[:rows, :cb] = s
+    return pad.reshape(rt, 4, 32, ct, 4).transpose(0, 3, 2, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("rows,cb", [(1, 1), (128, 4), (129, 5), (300, 7), (256, 512), (77, 260)])
+def test_swizzle_matches_the_tensor_reshape_form(rows, cb):
+    rng = np.random.default_rng(rows * 1000 + cb)
+    s = rng.integers(1, 255, (rows, cb), dtype=np.uint8)
+    out = oracle.swizzle_scales(s)
+    assert out.size == oracle.swizzled_scale_bytes(rows, cb) == (-(-rows // 128)) * (-(-cb // 4)) * 512
+    assert np.array_equal(out, _swizzle_by_reshape(s))
+    # every scale appears exactly once; the rest is zero padding
+    assert np.count_nonzero(out) == rows * cb
+
+
+def test_swizzle_worked_positions():
+    """Hand-placed entries: a 256 x 8 scale matrix has 2 x 2 tiles."""
+    s = np.zeros((256, 8), dtype=np.uint8)
+    s[0, 0], s[33, 5], s[127, 3], s[128, 0], s[255, 7], s[40, 4] = 1, 2, 3, 4, 5, 6
+    out = oracle.swizzle_scales(s)
+    assert out[0] == 1
+    assert out[512 + 16 * 1 + 4 * 1 + 1] == 2        # tile (0,1), j=1, i=1, k=1
+    assert out[16 * 31 + 4 * 3 + 3] == 3             # last byte of tile (0,0)
+    assert out[2 * 512] == 4                         # tile (1,0) starts the second tile row
+    assert out[4 * 512 - 1] == 5                     # last byte of tile (1,1)
+    assert out[512 + 16 * 8 + 4 * 1 + 0] == 6        # row 40: j=8, i=1; column 4: k=0

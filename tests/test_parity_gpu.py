@@ -386,3 +386,58 @@ def test_dequant_small_shapes(nv, rows, cols, rotate):
     yd = oracle.dequant_f64(q.cpu().numpy(), s.cpu().numpy(), float(g.cpu()[0]), rotate)
     tol = 1e-6 * np.abs(yd).reshape(-1, 16).max(1).repeat(16).reshape(yd.shape)
     assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - yd) <= tol)
+
+
+# ---------------------------------------------------------------- swizzled scales
+
+SWZ_SHAPES = [(1, 16), (3, 48), (127, 16), (128, 64), (129, 80), (300, 4112), (257, 8192)]
+
+
+@pytest.mark.parametrize("rows,cols", SWZ_SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swizzled_scales(nv, rows, cols, dtype):
+    """Scales written in the tiled layout equal the oracle's row-major scales
+    put through the oracle's layout map (zero padding included); codes, g and
+    amax equal the row-major call's."""
+    x = mixed_input(rows, cols, dtype, seed=rows * 3 + cols)
+    xd = to_dev(x)
+    q, s, g, a = nv.rotquant_swizzled(xd, rotate=True)
+    torch.cuda.synchronize()
+    oq, os_, og, oa = oracle.quantize(x, True)
+    compare(f"swizzled {rows}x{cols} {dtype}", x, True, (q, os_, g, a), (oq, os_, og, oa))
+    assert np.array_equal(s.cpu().numpy(), oracle.swizzle_scales(os_))
+
+
+@pytest.mark.parametrize("name,rotate", WORKLOAD_CASES)
+def test_swizzled_scales_full_size(nv, name, rotate):
+    w = synth.make(name, rotate=rotate)
+    xd = to_dev(w.x)
+    q, s, g, a = nv.rotquant_swizzled(xd, rotate=rotate)
+    rq, rs, rg, ra = nv.rotquant(xd, rotate=rotate)
+    torch.cuda.synchronize()
+    assert torch.equal(q, rq) and torch.equal(g, rg) and torch.equal(a, ra)
+    assert np.array_equal(s.cpu().numpy(), oracle.swizzle_scales(rs.cpu().numpy()))
+
+
+def test_swizzled_padding_is_rewritten_to_zero(nv):
+    x = mixed_input(129, 80, "bf16", seed=4)
+    xd = to_dev(x)
+    q, s, g, a = nv.rotquant_swizzled(xd)
+    s.fill_(0xAB)
+    nv.rotquant_swizzled(xd, out=(q, s, g, a))
+    torch.cuda.synchronize()
+    oq, os_, og, oa = oracle.quantize(x, True)
+    assert np.array_equal(s.cpu().numpy(), oracle.swizzle_scales(os_))
+
+
+@pytest.mark.parametrize("rows,cols", [(129, 80), (257, 8192)])
+def test_swizzled_dequant(nv, rows, cols):
+    x = mixed_input(rows, cols, "bf16", seed=rows + 2 * cols)
+    xd = to_dev(x)
+    for rotate in (True, False):
+        q, s, g, a = nv.rotquant_swizzled(xd, rotate=rotate)
+        y = nv.dequant_swizzled(q, s, g, rotate=rotate)
+        rq, rs, rg, ra = nv.rotquant(xd, rotate=rotate)
+        y_ref = nv.dequant(rq, rs, rg, rotate=rotate)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)

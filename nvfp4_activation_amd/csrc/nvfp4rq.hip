@@ -188,34 +188,55 @@ __global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __re
 // stored tile-row by tile-row, and S[128 rt + 32 i + j][4 ct + k] at byte
 // 512 (rt * ctiles + ct) + 16 j + 4 i + k.  Block indices fit in 32 bits
 // (checked on the host).
+// Each policy also fixes which blocks a pass-2 workgroup handles together
+// (a chunk): kSub groups of kThreads blocks.  Row-major: 256 consecutive
+// blocks.  Swizzled: a super-tile of 128 rows x 16 blocks, so that one
+// workgroup writes whole 512-byte scale tiles and whole 128-byte lines of
+// codes (lines completed from several L2s are written back piecemeal).
 struct RowMajorScales {
+  static constexpr int kSub = 1;
+  static constexpr bool kStaged = false;
   __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
+  __host__ __device__ int64_t chunks(int64_t nb) const { return (nb + kThreads - 1) / kThreads; }
+  __device__ __forceinline__ bool locate(int64_t chunk, int, uint32_t tid, int64_t nb, int64_t* b,
+                                         int64_t* si) const {
+    *b = chunk * kThreads + tid;
+    *si = *b;
+    return *b < nb;
+  }
 };
 struct SwizzledScales {
-  uint32_t cb, ctiles;  // blocks per row, ceil(cb / 4)
-  __device__ __forceinline__ int64_t operator()(int64_t b) const {
-    const uint32_t bb = static_cast<uint32_t>(b);
-    const uint32_t r = bb / cb, c = bb - r * cb;
+  static constexpr int kSub = 8;
+  static constexpr bool kStaged = true;  // scale tiles assembled in LDS
+  int64_t rows;
+  uint32_t cb, ctiles, cs;  // blocks per row, ceil(cb / 4), ceil(cb / 16)
+  __device__ __forceinline__ static int64_t place(uint32_t r, uint32_t c, uint32_t ctiles) {
     const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
     return static_cast<int64_t>(tile * 512u + (((r & 31u) << 4) | (((r >> 5) & 3u) << 2) | (c & 3u)));
   }
-};
-
-// Zero the bytes of a swizzled scale buffer that belong to no block (rows
-// past the last one, columns past cb): launched only when such padding exists.
-__global__ __launch_bounds__(kThreads) void swizzle_pad_kernel(uint8_t* __restrict__ s, int64_t rows,
-                                                               uint32_t cb, uint32_t ctiles,
-                                                               int64_t total) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total; i += stride) {
-    const int64_t tile = i >> 9;
-    const uint32_t inner = static_cast<uint32_t>(i & 511);
-    const int64_t rt = tile / ctiles, ct = tile - rt * ctiles;
-    const int64_t r = rt * 128 + ((inner >> 2) & 3u) * 32 + (inner >> 4);
-    const int64_t c = ct * 4 + (inner & 3u);
-    if (r >= rows || c >= cb) s[i] = 0;
+  __device__ __forceinline__ int64_t operator()(int64_t b) const {
+    const uint32_t bb = static_cast<uint32_t>(b);
+    const uint32_t r = bb / cb;
+    return place(r, bb - r * cb, ctiles);
   }
-}
+  __host__ __device__ int64_t chunks(int64_t) const { return ((rows + 127) / 128) * cs; }
+  __device__ __forceinline__ bool locate(int64_t chunk, int sub, uint32_t tid, int64_t, int64_t* b,
+                                         int64_t* si) const {
+    const int64_t rt = chunk / cs;
+    const uint32_t r = static_cast<uint32_t>(rt * 128 + sub * 16 + (tid >> 4));
+    const uint32_t c = static_cast<uint32_t>(chunk - rt * cs) * 16 + (tid & 15u);
+    if (r >= rows || c >= cb) return false;
+    *b = static_cast<int64_t>(r) * cb + c;
+    *si = place(r & 127u, c & 15u, 4);  // byte within the chunk's tiles
+    return true;
+  }
+  // The chunk's tiles (rt, 4 c16 .. 4 c16 + 3) are consecutive in memory.
+  __device__ __forceinline__ void chunk_tiles(int64_t chunk, int64_t* first_byte, int* ntiles) const {
+    const int64_t rt = chunk / cs, ct0 = (chunk - rt * cs) * 4;
+    *first_byte = (rt * ctiles + ct0) * 512;
+    *ntiles = static_cast<int>(ctiles - ct0 < 4 ? ctiles - ct0 : 4);
+  }
+};
 
 // Pass 2 body: each lane rotates, scales and encodes one block per iteration.
 // Workgroup w handles the 256-block chunks w, w + G, w + 2G, ... (G = grid
@@ -236,12 +257,20 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
                                              const float2* __restrict__ tab,
                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                              SMAP smap) {
-  const int64_t nchunks = (nb + kThreads - 1) / kThreads;
+  const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
+  __shared__ uint32_t stage[SMAP::kStaged ? 512 : 1];  // 4 scale tiles
   for (int64_t it = mine - 1; it >= 0; --it) {
-    const int64_t b = (it * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
-    if (b >= nb) continue;
+   const int64_t chunk = it * gridDim.x + blockIdx.x;
+   if constexpr (SMAP::kStaged) {
+     for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
+     __syncthreads();
+   }
+#pragma unroll 1
+   for (int sub = 0; sub < SMAP::kSub; ++sub) {
+    int64_t b, si;
+    if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
     float lo[8], hi[8];
     load_block(x, b, lo, hi);
     if (ROTATE) {
@@ -297,7 +326,22 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
       }
     }
     *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
-    s[smap(b)] = static_cast<uint8_t>(sb);
+    if constexpr (SMAP::kStaged)
+      reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
+    else
+      s[si] = static_cast<uint8_t>(sb);
+   }
+   if constexpr (SMAP::kStaged) {
+     // whole tiles, padding zeros included, in one coalesced store
+     __syncthreads();
+     int64_t first;
+     int ntiles;
+     smap.chunk_tiles(chunk, &first, &ntiles);
+     uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
+     for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
+       dst[i] = stage[i];
+     __syncthreads();
+   }
   }
 }
 
@@ -684,7 +728,7 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const float* amax
                            uint8_t* s, float* g, hipStream_t st, SMAP smap = SMAP{}) {
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(amax);
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
-  const dim3 grid(quant_grid(nb));
+  const dim3 grid(quant_grid(smap.chunks(nb) * kThreads));
   const hipError_t e =
       rotate ? launch(rotquant_kernel<T, true, SMAP>, grid, dim3(kThreads), st, x, nb, bits, allow_fast,
                       q, s, g, smap)
@@ -711,14 +755,10 @@ nvfp4_status rotquant_swizzled(const T* x, int64_t rows, int64_t cols, int rotat
   nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, false, sbytes);
   if (r != NVFP4_OK) return r;
   const uint32_t cb = static_cast<uint32_t>(cols / 16), ctiles = (cb + 3) / 4;
-  if (nb != 0 && (rows % 128 != 0 || cb % 4 != 0)) {
-    if (launch(swizzle_pad_kernel, dim3(generic_grid(sbytes)), dim3(kThreads), st, s, rows, cb, ctiles,
-               sbytes) != hipSuccess)
-      return NVFP4_ERR_HIP;
-  }
   r = enqueue_rotamax(x, nb, rotate, amax, st);
   if (r != NVFP4_OK) return r;
-  return enqueue_quant(x, nb, rotate, amax, q, s, g, st, SwizzledScales{cb, ctiles});
+  return enqueue_quant(x, nb, rotate, amax, q, s, g, st,
+                       SwizzledScales{rows, cb, ctiles, (cb + 15) / 16});
 }
 
 template <typename T>
@@ -887,7 +927,7 @@ nvfp4_status nvfp4_dequant_swizzled(const uint8_t* q, const uint8_t* s, const fl
   if (sbytes < 0) return NVFP4_ERR_SHAPE;
   const uint32_t cb = static_cast<uint32_t>(cols / 16);
   return dequant(q, s, gscale, rows, cols, rotate, y_out, stream, sbytes,
-                 SwizzledScales{cb, (cb + 3) / 4});
+                 SwizzledScales{rows, cb, (cb + 3) / 4, (cb + 15) / 16});
 }
 
 nvfp4_status nvfp4_rotate16(const uint16_t* x_bf16, int64_t rows, int64_t cols, float* y_out,

@@ -441,3 +441,20 @@ def test_swizzled_dequant(nv, rows, cols):
         y_ref = nv.dequant(rq, rs, rg, rotate=rotate)
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref)
+
+
+def test_swizzled_launch_shape_invariance(nv, monkeypatch):
+    """Super-tile chunks handed out over any number of workgroups give the
+    same bytes (ragged tile edges included)."""
+    x = mixed_input(300, 4112, "bf16", seed=8)
+    xd = to_dev(x)
+    ref = [t.clone() for t in nv.rotquant_swizzled(xd)]
+    torch.cuda.synchronize()
+    oq, os_, og, oa = oracle.quantize(x, True)
+    assert np.array_equal(ref[1].cpu().numpy(), oracle.swizzle_scales(os_))
+    for wgs in (1, 3, 7, 64, 100000):
+        monkeypatch.setenv("NVFP4RQ_QUANT_WGS", str(wgs))
+        got = nv.rotquant_swizzled(xd)
+        torch.cuda.synchronize()
+        for r, g in zip(ref, got):
+            assert torch.equal(r, g), wgs

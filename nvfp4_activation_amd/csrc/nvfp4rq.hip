@@ -49,6 +49,18 @@ constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
 // (possible only when the global scale comes from another tensor's amax) take
 // true divisions.
 constexpr float kQuotientLimit = 0x1p100f;
+// Arrival counters of the quantize pass when pass 1 leaves its partial maxima
+// in q_out: spread over kCounters words on separate 128-byte lines, since
+// thousands of increments of one word serialize (and a workgroup's loads
+// wait behind its own pending atomic).
+constexpr int kCounters = 64;
+constexpr int kCounterStride = 32;  // words
+__host__ __device__ constexpr int64_t counter_base(int64_t npartials) {
+  return (npartials + kCounterStride - 1) / kCounterStride * kCounterStride;  // words
+}
+__host__ __device__ constexpr int64_t head_bytes(int64_t npartials) {
+  return 4 * (counter_base(npartials) + kCounters * kCounterStride);
+}
 
 // ---------------------------------------------------------------- reductions
 
@@ -61,10 +73,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
   return u;
 }
 
-// Workgroup maximum, then one atomicMax per workgroup.  Non-negative binary32
+// Workgroup maximum, then either one atomicMax per workgroup on a zeroed word
+// (partials == 0), or a plain store of the workgroup's maximum to out[wg]
+// (partials == 1; workgroup 0 also clears the arrival counters the quantize
+// pass uses, so no word has to be zeroed beforehand).  Non-negative binary32
 // values order like their bit patterns, so the maximum is exact and the same
 // for any reduction order (a NaN input stays visible as bits above +inf).
-__device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restrict__ out) {
+__device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restrict__ out,
+                                                 int partials) {
   __shared__ uint32_t part[kThreads / 64];
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
@@ -73,8 +89,13 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restric
     uint32_t r = part[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) r = umax(r, part[i]);
-    atomicMax(out, r);
+    if (partials)
+      out[blockIdx.x] = r;
+    else
+      atomicMax(out, r);
   }
+  if (partials && blockIdx.x == 0 && threadIdx.x < kCounters)
+    out[counter_base(gridDim.x) + threadIdx.x * kCounterStride] = 0u;
 }
 
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
@@ -97,7 +118,8 @@ __global__ void zero_word_kernel(uint32_t* __restrict__ w) { *w = 0u; }
 template <bool ROTATE>
 __global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 int64_t nb,
-                                                                uint32_t* __restrict__ amax_bits) {
+                                                                uint32_t* __restrict__ amax_bits,
+                                                                int partials) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
@@ -133,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* 
     }
   }
   if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
-  workgroup_max_to(m, amax_bits);
+  workgroup_max_to(m, amax_bits, partials);
 }
 
 // One 16-value fp32 block: elements 0..7 into lo, 8..15 into hi.
@@ -159,7 +181,8 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
 template <bool ROTATE>
 __global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __restrict__ x,
                                                                int64_t nb,
-                                                               uint32_t* __restrict__ amax_bits) {
+                                                               uint32_t* __restrict__ amax_bits,
+                                                               int partials) {
   uint32_t m = 0u;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb; b += stride) {
@@ -177,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __re
     }
   }
   if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
-  workgroup_max_to(m, amax_bits);
+  workgroup_max_to(m, amax_bits, partials);
 }
 
 // Where block b's scale byte is stored.  Row-major: byte b of the
@@ -198,6 +221,7 @@ struct RowMajorScales {
   static constexpr bool kStaged = false;
   __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
   __host__ __device__ int64_t chunks(int64_t nb) const { return (nb + kThreads - 1) / kThreads; }
+  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const { return chunk * kThreads * 8; }
   __device__ __forceinline__ bool locate(int64_t chunk, int, uint32_t tid, int64_t nb, int64_t* b,
                                          int64_t* si) const {
     *b = chunk * kThreads + tid;
@@ -210,6 +234,10 @@ struct SwizzledScales {
   static constexpr bool kStaged = true;  // scale tiles assembled in LDS
   int64_t rows;
   uint32_t cb, ctiles, cs;  // blocks per row, ceil(cb / 4), ceil(cb / 16)
+  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const {
+    const int64_t rt = chunk / cs;
+    return (rt * 128 * cb + (chunk - rt * cs) * 16) * 8;
+  }
   __device__ __forceinline__ static int64_t place(uint32_t r, uint32_t c, uint32_t ctiles) {
     const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
     return static_cast<int64_t>(tile * 512u + (((r & 31u) << 4) | (((r >> 5) & 3u) << 2) | (c & 3u)));
@@ -238,6 +266,47 @@ struct SwizzledScales {
   }
 };
 
+// When pass 1 leaves its per-workgroup maxima at the head of q_out, every
+// pass-2 workgroup reads them in its prologue and then counts itself in; a
+// workgroup waits for all of them to have done so before it writes a chunk
+// whose codes reach into that head.  Chunks run last-first, so the wait comes
+// at the end of the few workgroups concerned, and since the others never wait
+// the count always completes.  The wait is bounded: past spin_limit sleeps the
+// workgroup goes on and marks the call failed with a NaN global scale.
+struct HeadGuard {
+  uint32_t* counters;  // null: no partials in q_out
+  int64_t bytes;       // head bytes holding partials and counters
+  uint32_t need;       // pass-2 workgroups
+  uint32_t spin_limit;
+  float* gscale_out;
+};
+
+__device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
+  __shared__ int timed_out;
+  if (threadIdx.x < 64) {  // wave 0: one counter per lane
+    uint32_t spins = 0;
+    int late = 0;
+    // Relaxed: acquire/release at agent scope would write back or invalidate
+    // the L2 of every XCD involved on each poll.  Nothing written by other
+    // workgroups is read after the wait; the waiter's stores follow the loop.
+    for (;;) {
+      uint32_t c = __hip_atomic_load(h.counters + threadIdx.x * kCounterStride, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
+      if (c >= h.need) break;
+      if (++spins > h.spin_limit) {
+        late = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (threadIdx.x == 0) timed_out = late;
+  }
+  __syncthreads();
+  if (timed_out && threadIdx.x == 0) *h.gscale_out = __uint_as_float(0x7FC00000u);
+}
+
 // Pass 2 body: each lane rotates, scales and encodes one block per iteration.
 // Workgroup w handles the 256-block chunks w, w + G, w + 2G, ... (G = grid
 // size), last chunk first: the chunks pass 1 read last are the likeliest to
@@ -256,13 +325,14 @@ template <typename T, bool ROTATE, bool FAST, typename SMAP>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
                                              const float2* __restrict__ tab,
                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                             SMAP smap) {
+                                             SMAP smap, const HeadGuard& head) {
   const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
   __shared__ uint32_t stage[SMAP::kStaged ? 512 : 1];  // 4 scale tiles
   for (int64_t it = mine - 1; it >= 0; --it) {
    const int64_t chunk = it * gridDim.x + blockIdx.x;
+   if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
    if constexpr (SMAP::kStaged) {
      for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
      __syncthreads();
@@ -345,16 +415,43 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
   }
 }
 
+// amax_src: the amax word (npartials == 0) or pass 1's per-workgroup maxima
+// at the head of q (npartials of them, then the counter; amax_out receives
+// their maximum).
 template <typename T, bool ROTATE, typename SMAP>
 __global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
-                                                            const uint32_t* __restrict__ amax_bits,
-                                                            int allow_fast,
+                                                            const uint32_t* amax_src,
+                                                            int npartials, float* __restrict__ amax_out,
+                                                            uint32_t spin_limit, int allow_fast,
                                                             uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ s,
                                                             float* __restrict__ gscale_out,
                                                             SMAP smap) {
   __shared__ float2 tab[128];
-  const uint32_t abits = *amax_bits;
+  __shared__ uint32_t red[kThreads / 64];
+  HeadGuard head{nullptr, 0, 0, spin_limit, gscale_out};
+  uint32_t abits;
+  if (npartials == 0) {
+    abits = *amax_src;
+  } else {
+    uint32_t m = 0u;
+    for (int i = threadIdx.x; i < npartials; i += kThreads) m = umax(m, amax_src[i]);
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    abits = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) abits = umax(abits, red[i]);
+    uint32_t* counters = const_cast<uint32_t*>(amax_src) + counter_base(npartials);
+    // every thread's read of the partials is complete (their values met at
+    // the barrier) before the workgroup counts itself in; a relaxed increment
+    // needs no cache write-back
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *amax_out = __uint_as_float(abits);
+    head = HeadGuard{counters, head_bytes(npartials), gridDim.x, spin_limit, gscale_out};
+  }
   const float g = global_scale(__uint_as_float(abits));
   if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
   if constexpr (sizeof(T) == 2) {
@@ -366,11 +463,11 @@ __global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict_
         tab[threadIdx.x] = make_float2(d, 1.0f / d);
       }
       __syncthreads();
-      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap);
+      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head);
       return;
     }
   }
-  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap);
+  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head);
 }
 
 // Kernels that write fp32 per element (decode, rotation alone) use a
@@ -696,23 +793,23 @@ nvfp4_status validate_quant(const T* x, int64_t rows, int64_t cols, int rotate, 
   return NVFP4_OK;
 }
 
-template <typename T>
-hipError_t launch_rotamax(const T* x, int64_t nb, int rotate, uint32_t* bits, hipStream_t st);
+// partials == 1: pass 1 stores its per-workgroup maxima (and a cleared
+// counter) at bits[0 .. grid] instead of an atomicMax into bits[0].
+int amax_grid_for(const uint16_t*, int64_t nb) { return amax_grid(nb, true); }
+int amax_grid_for(const float*, int64_t nb) { return amax_grid(nb, false); }
 
-template <>
-hipError_t launch_rotamax<uint16_t>(const uint16_t* x, int64_t nb, int rotate, uint32_t* bits,
-                                    hipStream_t st) {
+hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* bits, int partials,
+                          hipStream_t st) {
   const dim3 grid(amax_grid(nb, true));
-  return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits)
-                : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits);
+  return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials)
+                : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials);
 }
 
-template <>
-hipError_t launch_rotamax<float>(const float* x, int64_t nb, int rotate, uint32_t* bits,
-                                 hipStream_t st) {
+hipError_t launch_rotamax(const float* x, int64_t nb, int rotate, uint32_t* bits, int partials,
+                          hipStream_t st) {
   const dim3 grid(amax_grid(nb, false));
-  return rotate ? launch(rotamax_f32_kernel<true>, grid, dim3(kThreads), st, x, nb, bits)
-                : launch(rotamax_f32_kernel<false>, grid, dim3(kThreads), st, x, nb, bits);
+  return rotate ? launch(rotamax_f32_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials)
+                : launch(rotamax_f32_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials);
 }
 
 template <typename T>
@@ -720,21 +817,45 @@ nvfp4_status enqueue_rotamax(const T* x, int64_t nb, int rotate, float* amax, hi
   uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
   if (launch(zero_word_kernel, dim3(1), dim3(1), st, bits) != hipSuccess) return NVFP4_ERR_HIP;
   if (nb == 0) return NVFP4_OK;
-  return launch_rotamax(x, nb, rotate, bits, st) == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+  return launch_rotamax(x, nb, rotate, bits, 0, st) == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+// Pass 2.  npartials == 0: the amax is the word at amax_src.  Otherwise
+// amax_src holds npartials per-workgroup maxima and the counter (at the head
+// of q) and the kernel writes their maximum to amax_out.
 template <typename T, typename SMAP = RowMajorScales>
-nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const float* amax, uint8_t* q,
-                           uint8_t* s, float* g, hipStream_t st, SMAP smap = SMAP{}) {
-  const uint32_t* bits = reinterpret_cast<const uint32_t*>(amax);
+nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const uint32_t* amax_src,
+                           int npartials, float* amax_out, uint8_t* q, uint8_t* s, float* g,
+                           hipStream_t st, SMAP smap = SMAP{}) {
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
+  const int64_t spin_env = env_int("NVFP4RQ_SPIN_LIMIT");
+  const uint32_t spin_limit = spin_env > 0 ? static_cast<uint32_t>(spin_env) : (1u << 26);
   const dim3 grid(quant_grid(smap.chunks(nb) * kThreads));
   const hipError_t e =
-      rotate ? launch(rotquant_kernel<T, true, SMAP>, grid, dim3(kThreads), st, x, nb, bits, allow_fast,
-                      q, s, g, smap)
-             : launch(rotquant_kernel<T, false, SMAP>, grid, dim3(kThreads), st, x, nb, bits,
-                      allow_fast, q, s, g, smap);
+      rotate ? launch(rotquant_kernel<T, true, SMAP>, grid, dim3(kThreads), st, x, nb, amax_src,
+                      npartials, amax_out, spin_limit, allow_fast, q, s, g, smap)
+             : launch(rotquant_kernel<T, false, SMAP>, grid, dim3(kThreads), st, x, nb, amax_src,
+                      npartials, amax_out, spin_limit, allow_fast, q, s, g, smap);
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+// Both passes.  When q_out has room (8 nb bytes against head_bytes: from
+// about 1040 blocks up), pass 1 leaves per-workgroup maxima and cleared counters at
+// the head of q_out (which pass 2 overwrites last), so no word has to be
+// zeroed first; smaller tensors take the zeroed-word path.
+template <typename T, typename SMAP = RowMajorScales>
+nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_t* s, float* g,
+                          float* amax, hipStream_t st, SMAP smap = SMAP{}) {
+  const int g1 = amax_grid_for(x, nb);
+  if (nb == 0 || head_bytes(g1) > 8 * nb || env_int("NVFP4RQ_ZEROED_AMAX")) {
+    nvfp4_status r = enqueue_rotamax(x, nb, rotate, amax, st);
+    if (r != NVFP4_OK) return r;
+    return enqueue_quant(x, nb, rotate, reinterpret_cast<const uint32_t*>(amax), 0, amax, q, s, g, st,
+                         smap);
+  }
+  uint32_t* head = reinterpret_cast<uint32_t*>(q);
+  if (launch_rotamax(x, nb, rotate, head, 1, st) != hipSuccess) return NVFP4_ERR_HIP;
+  return enqueue_quant(x, nb, rotate, head, g1, amax, q, s, g, st, smap);
 }
 
 // Size of the swizzled scale buffer for a [rows, cols] tensor; -1 for a bad
@@ -755,10 +876,7 @@ nvfp4_status rotquant_swizzled(const T* x, int64_t rows, int64_t cols, int rotat
   nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, false, sbytes);
   if (r != NVFP4_OK) return r;
   const uint32_t cb = static_cast<uint32_t>(cols / 16), ctiles = (cb + 3) / 4;
-  r = enqueue_rotamax(x, nb, rotate, amax, st);
-  if (r != NVFP4_OK) return r;
-  return enqueue_quant(x, nb, rotate, amax, q, s, g, st,
-                       SwizzledScales{rows, cb, ctiles, (cb + 15) / 16});
+  return enqueue_both(x, nb, rotate, q, s, g, amax, st, SwizzledScales{rows, cb, ctiles, (cb + 15) / 16});
 }
 
 template <typename T>
@@ -767,9 +885,7 @@ nvfp4_status rotquant(const T* x, int64_t rows, int64_t cols, int rotate, uint8_
   int64_t nb = 0;
   nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, false);
   if (r != NVFP4_OK) return r;
-  r = enqueue_rotamax(x, nb, rotate, amax, st);
-  if (r != NVFP4_OK) return r;
-  return enqueue_quant(x, nb, rotate, amax, q, s, g, st);
+  return enqueue_both(x, nb, rotate, q, s, g, amax, st);
 }
 
 template <typename T>
@@ -794,7 +910,8 @@ nvfp4_status quant_from_amax(const T* x, int64_t rows, int64_t cols, int rotate,
   int64_t nb = 0;
   nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, true);
   if (r != NVFP4_OK) return r;
-  return enqueue_quant(x, nb, rotate, amax, q, s, g, st);
+  return enqueue_quant(x, nb, rotate, reinterpret_cast<const uint32_t*>(amax), 0, nullptr, q, s, g,
+                       st);
 }
 
 

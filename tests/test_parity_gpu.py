@@ -458,3 +458,46 @@ def test_swizzled_launch_shape_invariance(nv, monkeypatch):
         torch.cuda.synchronize()
         for r, g in zip(ref, got):
             assert torch.equal(r, g), wgs
+
+
+# ---------------------------------------------------------------- pass-1 partials in q_out
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_partials_path_equals_zeroed_word_path(nv, monkeypatch, dtype):
+    """The fused call keeps pass 1's per-workgroup maxima at the head of q_out
+    (no zeroed word); forcing the zeroed-word path gives the same bytes, for
+    every pass-2 grid size and for the swizzled layout too."""
+    x = mixed_input(777, 2064, dtype, seed=31)
+    xd = to_dev(x)
+    for rotate in (True, False):
+        a = [t.clone() for t in nv.rotquant(xd, rotate=rotate)]
+        sa = [t.clone() for t in nv.rotquant_swizzled(xd, rotate=rotate)]
+        torch.cuda.synchronize()
+        compare(f"partials {dtype} rotate={rotate}", x, rotate, a)
+        monkeypatch.setenv("NVFP4RQ_ZEROED_AMAX", "1")
+        b = nv.rotquant(xd, rotate=rotate)
+        sb = nv.rotquant_swizzled(xd, rotate=rotate)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("NVFP4RQ_ZEROED_AMAX")
+        for u, v in zip(a + sa, list(b) + list(sb)):
+            assert torch.equal(u, v)
+    for a_wgs, q_wgs in ((1, 1), (1000, 1), (3, 2048), (700, 5)):
+        monkeypatch.setenv("NVFP4RQ_AMAX_WGS", str(a_wgs))
+        monkeypatch.setenv("NVFP4RQ_QUANT_WGS", str(q_wgs))
+        got = nv.rotquant(xd)
+        torch.cuda.synchronize()
+        compare(f"partials {dtype} grids {a_wgs}/{q_wgs}", x, True, got)
+
+
+def test_head_wait_with_tiny_spin_limit(nv, monkeypatch):
+    """A spin limit of one sleep: the wait either completes in time (output
+    equal to the oracle) or gives up and marks the call with a NaN scale;
+    either way every workgroup exits."""
+    monkeypatch.setenv("NVFP4RQ_SPIN_LIMIT", "1")
+    x = mixed_input(1024, 4096, "bf16", seed=12)
+    xd = to_dev(x)
+    for _ in range(3):
+        q, s, g, a = nv.rotquant(xd)
+        torch.cuda.synchronize()
+        if not np.isnan(g.cpu().numpy()[0]):
+            compare("tiny spin limit", x, True, (q, s, g, a))

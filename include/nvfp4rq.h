@@ -145,6 +145,27 @@ nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gsca
                            hipStream_t stream);
 
 /*
+ * Measurement hook: nvfp4_rotquant (bf16), with every kernel it launches
+ * timed by HIP events that the runtime records at that kernel's own start and
+ * end (hipExtLaunchKernel), so that a caller can time each pass of the fused
+ * call in place, without the dispatch gap an event between launches adds.
+ *   events    npairs * 2 created events (hipEventCreate, or torch events that
+ *             have been recorded once); the k-th kernel launched records
+ *             events[2k] and events[2k + 1]; kernels past npairs are not
+ *             timed.
+ *   nkernels  receives the number of kernels launched: 2 (amax pass,
+ *             quantize pass) when q_out has room for pass 1's partial maxima,
+ *             3 (zeroing, amax, quantize) for small tensors, 1 or 2 for
+ *             empty ones.
+ * Results are those of nvfp4_rotquant.  NVFP4_ERR_NULL when events or
+ * nkernels is NULL or npairs < 1.
+ */
+nvfp4_status nvfp4_rotquant_timed(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,
+                                  uint8_t *q_out, uint8_t *s_out, float *gscale_out,
+                                  float *amax_out, hipStream_t stream, hipEvent_t *events,
+                                  int npairs, int *nkernels);
+
+/*
  * Block scales in the swizzled tiled layout (page "A Fused Hadamard + NVFP4
  * Quantization Kernel in Triton", section 6: GEMMs read scales tiled, and a
  * production kernel writes that layout itself).  The page does not give the

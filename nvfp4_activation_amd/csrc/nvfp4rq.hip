@@ -678,12 +678,25 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __r
 
 // ---------------------------------------------------------------- host helpers
 
+// Timing hook of the *_timed entry points: while one runs on this thread, its
+// k-th launch (k = 0, 1, ...) goes through hipExtLaunchKernel, which records
+// events[2k] when the kernel starts and events[2k + 1] when it ends.
+thread_local hipEvent_t* t_events = nullptr;
+thread_local int t_pairs = 0;
+thread_local int t_launched = 0;
+
 // hipLaunchKernel with the kernel's own parameter types; returns the launch status.
 template <typename... KArgs, typename... Args, size_t... I>
 hipError_t launch_impl(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
                        std::index_sequence<I...>, Args... args) {
   std::tuple<KArgs...> t(static_cast<KArgs>(args)...);
   void* argv[] = {static_cast<void*>(&std::get<I>(t))..., nullptr};
+  if (t_events) {
+    const int n = t_launched++;
+    if (n < t_pairs)
+      return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, st,
+                                t_events[2 * n], t_events[2 * n + 1], 0);
+  }
   return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, st);
 }
 
@@ -988,6 +1001,23 @@ nvfp4_status nvfp4_rotquant(const uint16_t* x_bf16, int64_t rows, int64_t cols, 
                             uint8_t* q_out, uint8_t* s_out, float* gscale_out, float* amax_out,
                             hipStream_t stream) {
   return rotquant(x_bf16, rows, cols, rotate, q_out, s_out, gscale_out, amax_out, stream);
+}
+
+nvfp4_status nvfp4_rotquant_timed(const uint16_t* x_bf16, int64_t rows, int64_t cols, int rotate,
+                                  uint8_t* q_out, uint8_t* s_out, float* gscale_out,
+                                  float* amax_out, hipStream_t stream, hipEvent_t* events,
+                                  int npairs, int* nkernels) {
+  if (!events || npairs < 1 || !nkernels) return NVFP4_ERR_NULL;
+  t_events = events;
+  t_pairs = npairs;
+  t_launched = 0;
+  const nvfp4_status r =
+      rotquant(x_bf16, rows, cols, rotate, q_out, s_out, gscale_out, amax_out, stream);
+  *nkernels = t_launched;
+  t_events = nullptr;
+  t_pairs = 0;
+  t_launched = 0;
+  return r;
 }
 
 nvfp4_status nvfp4_rotquant_f32(const float* x, int64_t rows, int64_t cols, int rotate,

@@ -41,6 +41,7 @@ def lib():
     for name in ("nvfp4_rotquant_swizzled", "nvfp4_rotquant_swizzled_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p]
     lib.nvfp4_dequant_swizzled.argtypes = [p, p, p, i64, i64, i, p, p]
+    lib.nvfp4_rotquant_timed.argtypes = [p, i64, i64, i, p, p, p, p, p, p, i, p]
     lib.nvfp4_swizzled_scale_bytes.argtypes = [i64, i64]
     lib.nvfp4_swizzled_scale_bytes.restype = i64
     lib.nvfp4_status_string.argtypes = [i]
@@ -55,7 +56,7 @@ def test_header_declares_the_boundary():
                  "mxfp4_rotquant", "mxfp4_rotquant_f32", "mxfp4_dequant",
                  "nvfp4_rotate16", "nvfp4_rotate16_f32", "nvfp4_rotquant_swizzled",
                  "nvfp4_rotquant_swizzled_f32", "nvfp4_dequant_swizzled",
-                 "nvfp4_swizzled_scale_bytes"):
+                 "nvfp4_swizzled_scale_bytes", "nvfp4_rotquant_timed"):
         assert must in names
 
 
@@ -220,3 +221,18 @@ def test_swizzled_dequant_validation(lib):
     assert f(Q, S, G, 4, 40, 1, Y, None) == ERR_SHAPE
     assert f(Q, S, G, 4, 64, 3, Y, None) == ERR_ARG
     assert f(Q, S, G, 4, 64, 1, S - 64, None) == ERR_ARG
+
+
+def test_timed_validation(lib):
+    """events and nkernels are host memory (an array of event handles and an
+    int); validation runs before any event is touched."""
+    f = lib.nvfp4_rotquant_timed
+    ev = (ctypes.c_void_p * 4)()
+    nk = ctypes.c_int(-1)
+    EV, NK = ctypes.addressof(ev), ctypes.addressof(nk)
+    assert f(X, 4, 64, 1, Q, S, G, A, None, None, 2, NK) == ERR_NULL
+    assert f(X, 4, 64, 1, Q, S, G, A, None, EV, 0, NK) == ERR_NULL
+    assert f(X, 4, 64, 1, Q, S, G, A, None, EV, 2, None) == ERR_NULL
+    assert f(X, 4, 40, 1, Q, S, G, A, None, EV, 2, NK) == ERR_SHAPE
+    assert nk.value == 0                     # nothing launched
+    assert f(X, 4, 64, 1, X, S, G, A, None, EV, 2, NK) == ERR_ARG

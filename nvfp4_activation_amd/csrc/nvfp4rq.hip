@@ -49,6 +49,7 @@ constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
 // (possible only when the global scale comes from another tensor's amax) take
 // true divisions.
 constexpr float kQuotientLimit = 0x1p100f;
+constexpr int64_t kLastLevelKeep = 176LL << 20;  // bytes of input pass 1 leaves cached
 // Arrival counters of the quantize pass when pass 1 leaves its partial maxima
 // in q_out: spread over kCounters words on separate 128-byte lines, since
 // thousands of increments of one word serialize (and a workgroup's loads
@@ -115,11 +116,17 @@ __global__ void zero_word_kernel(uint32_t* __restrict__ w) { *w = 0u; }
 // Both lanes compute the same sums; the maximum absorbs the duplicate.
 // max |0.25 z| = RN(0.25 max |z|) because rounding is monotone, so the scaling
 // is applied once at the end.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nontemporal(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <bool ROTATE>
 __global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 int64_t nb,
                                                                 uint32_t* __restrict__ amax_bits,
-                                                                int partials) {
+                                                                int partials, int64_t nt_end) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
@@ -129,7 +136,10 @@ __global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* 
   uint32_t m = 0u;
   for (int64_t base = wave * kPerWave; base < npieces; base += nwaves * kPerWave) {
     uint4 v[kAmaxPieces];
-    if (base + kPerWave <= npieces) {      // wave-uniform: every piece in range
+    if (base + kPerWave <= nt_end) {       // streamed past the caches (see launch_rotamax)
+#pragma unroll
+      for (int j = 0; j < kAmaxPieces; ++j) v[j] = load_nontemporal(p + base + j * 64 + lane);
+    } else if (base + kPerWave <= npieces) {  // wave-uniform: every piece in range
 #pragma unroll
       for (int j = 0; j < kAmaxPieces; ++j) v[j] = p[base + j * 64 + lane];
     } else {                               // the tensor's last, partial chunk
@@ -814,8 +824,18 @@ int amax_grid_for(const float*, int64_t nb) { return amax_grid(nb, false); }
 hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* bits, int partials,
                           hipStream_t st) {
   const dim3 grid(amax_grid(nb, true));
-  return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials)
-                : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials);
+  // The quantize pass walks the tensor last-first and finds the part pass 1
+  // read last in the 256 MB last-level cache; the part before the last
+  // kLastLevelKeep bytes would be evicted before the quantize pass got to it,
+  // so pass 1 streams it with non-temporal loads (measured at 16384 x 8192:
+  // 1 us off pass 1, nothing lost in pass 2; streaming more costs pass 2 its
+  // cache hits).
+  const int64_t keep_mb = env_int("NVFP4RQ_LLC_KEEP_MB");
+  const int64_t keep_pieces = (keep_mb ? keep_mb << 20 : kLastLevelKeep) / 16;
+  const int64_t nt_end = 2 * nb > keep_pieces ? 2 * nb - keep_pieces : 0;
+  return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials, nt_end)
+                : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials,
+                         nt_end);
 }
 
 hipError_t launch_rotamax(const float* x, int64_t nb, int rotate, uint32_t* bits, int partials,

@@ -78,13 +78,21 @@ typedef enum nvfp4_status {
  *   rotate      1: rotate each block by H16 before scaling; 0: no rotation.
  *   q_out       device, rows * cols / 2 bytes, 16-byte aligned: E2M1 codes,
  *               row-major [rows, cols/2], element 2k in the low nibble of
- *               byte k.  May be NULL when rows * cols == 0.
+ *               byte k.  May be NULL when rows * cols == 0.  The call first
+ *               keeps pass 1's per-workgroup maxima and arrival counters in
+ *               its first bytes (at least about 8 KiB, for tensors of about
+ *               1040 blocks or more), so its contents are defined only once
+ *               the call has completed on the stream.
  *   s_out       device, rows * cols / 16 bytes, 4-byte aligned: E4M3FN block
  *               scales (0x00..0x7E), row-major [rows, cols/16].  May be NULL
  *               when rows * cols == 0.
  *   gscale_out  device, 1 float, 4-byte aligned: the global scale s_global.
+ *               NaN if the quantize pass gave up waiting for its own
+ *               workgroups (a bounded wait that cannot run out while the
+ *               device schedules the grid).
  *   amax_out    device, 1 float, 4-byte aligned: the rotated global amax.
- *               Used as the pass-1 accumulator; zeroed by this call.
+ *               Written by this call (for small tensors it is zeroed and
+ *               used as the pass-1 accumulator).
  *   stream      HIP stream.
  * rows * cols == 0 is valid: it writes amax 0 and global scale 1.
  */

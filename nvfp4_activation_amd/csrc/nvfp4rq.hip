@@ -747,11 +747,14 @@ int clamp_grid(int64_t want, int64_t needed) {
   return static_cast<int>(g);
 }
 
-// Pass 1: 4 workgroups per compute unit, each wave streaming 8 KiB (bf16) per
-// iteration; fp32: one block per lane per iteration.
+// Pass 1: 2 workgroups per compute unit, each wave streaming 8 KiB (bf16) per
+// iteration; fp32: one block per lane per iteration.  Pass 1 alone runs
+// about as fast with 4 or 8 per CU, but every quantize workgroup of the fused
+// call reduces one maximum per pass-1 workgroup before it starts (measured
+// step at 16384 x 8192: 102.8 us with 2 per CU, 103.7 with 4, 103.2 with 8).
 int amax_grid(int64_t nb, bool bf16) {
   int64_t want = env_int("NVFP4RQ_AMAX_WGS");
-  if (!want) want = 4LL * device_cus();
+  if (!want) want = 2LL * device_cus();
   const int64_t per_wg = bf16 ? (kThreads / 64) * 64LL * kAmaxPieces / 2 : kThreads;  // blocks
   return clamp_grid(want, (nb + per_wg - 1) / per_wg);
 }

@@ -331,11 +331,57 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
 // 4 are exact there), the divisions are corrected reciprocal products and the
 // per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
 // Otherwise every division is a true binary32 division.
+// A lane's first block, loaded (as raw bits) before the kernel's prologue so
+// that the load latency overlaps the amax reduction and the table set-up.
+template <typename T>
+struct FirstBlock;
+template <>
+struct FirstBlock<uint16_t> {
+  uint4 a, b;
+  __device__ __forceinline__ void load(const uint16_t* x, int64_t blk) {
+    const uint4* p = reinterpret_cast<const uint4*>(x + blk * 16);
+    a = p[0];
+    b = p[1];
+  }
+  __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
+    widen8(a, lo);
+    widen8(b, hi);
+  }
+};
+template <>
+struct FirstBlock<float> {
+  float4 a, b, c, d;
+  __device__ __forceinline__ void load(const float* x, int64_t blk) {
+    const float4* p = reinterpret_cast<const float4*>(x + blk * 16);
+    a = p[0];
+    b = p[1];
+    c = p[2];
+    d = p[3];
+  }
+  __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
+    lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
+    lo[4] = b.x; lo[5] = b.y; lo[6] = b.z; lo[7] = b.w;
+    hi[0] = c.x; hi[1] = c.y; hi[2] = c.z; hi[3] = c.w;
+    hi[4] = d.x; hi[5] = d.y; hi[6] = d.z; hi[7] = d.w;
+  }
+};
+
+template <typename T, typename SMAP>
+__device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, SMAP smap,
+                                           FirstBlock<T>* f) {
+  const int64_t nchunks = smap.chunks(nb);
+  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  int64_t b, si;
+  if (mine > 0 && smap.locate((mine - 1) * gridDim.x + blockIdx.x, 0, threadIdx.x, nb, &b, &si))
+    f->load(x, b);
+}
+
 template <typename T, bool ROTATE, bool FAST, typename SMAP>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
                                              const float2* __restrict__ tab,
                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                             SMAP smap, const HeadGuard& head) {
+                                             SMAP smap, const HeadGuard& head,
+                                             const FirstBlock<T>& first) {
   const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
@@ -352,7 +398,11 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
     int64_t b, si;
     if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
     float lo[8], hi[8];
-    load_block(x, b, lo, hi);
+    if (!SMAP::kStaged && it == mine - 1 && sub == 0) {  // loaded before the prologue
+      first.unpack(lo, hi);
+    } else {
+      load_block(x, b, lo, hi);
+    }
     if (ROTATE) {
       stages_1_2_4(lo);
       stages_1_2_4(hi);
@@ -428,8 +478,9 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
 // amax_src: the amax word (npartials == 0) or pass 1's per-workgroup maxima
 // at the head of q (npartials of them, then the counter; amax_out receives
 // their maximum).
+// Eight workgroups per CU (the grid size assumes it): at most 64 VGPRs.
 template <typename T, bool ROTATE, typename SMAP>
-__global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
                                                             const uint32_t* amax_src,
                                                             int npartials, float* __restrict__ amax_out,
                                                             uint32_t spin_limit, int allow_fast,
@@ -439,6 +490,8 @@ __global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict_
                                                             SMAP smap) {
   __shared__ float2 tab[128];
   __shared__ uint32_t red[kThreads / 64];
+  FirstBlock<T> first;
+  if constexpr (!SMAP::kStaged) load_first(x, nb, smap, &first);  // staged: no registers to spare
   HeadGuard head{nullptr, 0, 0, spin_limit, gscale_out};
   uint32_t abits;
   if (npartials == 0) {
@@ -473,11 +526,11 @@ __global__ __launch_bounds__(kThreads) void rotquant_kernel(const T* __restrict_
         tab[threadIdx.x] = make_float2(d, 1.0f / d);
       }
       __syncthreads();
-      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head);
+      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head, first);
       return;
     }
   }
-  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head);
+  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head, first);
 }
 
 // Kernels that write fp32 per element (decode, rotation alone) use a

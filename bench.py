@@ -3,9 +3,10 @@
 Workload: a 16384 x 8192 bf16 activation tensor, Student-t (3 d.o.f.) values
 times per-column log-normal gains, rotation on (seeded synthetic data).
 
-One step = the whole hot path over the tensor: zero the amax word, pass 1
-(rotated global amax: reads 2 B per element), pass 2 (global scale, rotate,
-block scales, E2M1 codes: reads 2 B and writes 0.5625 B per element).
+One step = the whole hot path over the tensor, one call of the fused entry
+point: pass 1 (rotated global amax: reads 2 B per element), pass 2 (global
+scale, rotate, block scales, E2M1 codes: reads 2 B and writes 0.5625 B per
+element).
 Algorithmic bytes per step: 4.5625 B per element + 8 B.
 
 Timing: each timed step runs on torch's current stream between HIP events;
@@ -159,7 +160,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, each one call of the fused entry point
-    # (zero word + pass 1 + pass 2) between two events, after a cold() read.
+    # (pass 1 + pass 2) between two events, after a cold() read.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()

@@ -1,0 +1,109 @@
+// Launch constants, reductions and block loads shared by the kernels of
+// libnvfp4rq (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "nvfp4rq_device.hpp"
+
+namespace nvfp4rq {
+namespace {  // one translation unit (nvfp4rq.hip): internal linkage
+
+constexpr int kThreads = 256;      // 4 waves of 64
+constexpr int kAmaxPieces = 8;     // 16-byte pieces per lane per iteration in the bf16 amax pass
+
+// The fast path (corrected divisions with per-scale reciprocals) is used for
+// bf16 input when the global amax lies in [2^-38, 2^15): then every divisor is
+// in [2^-58.4, 2^14.4] and every quotient stays inside the range on which the
+// corrected division was enumerated.  Other tensors take the exact path
+// (IEEE divisions); both give identical bytes.
+constexpr uint32_t kFastAmaxLo = 0x2C800000u;   // 2^-38
+constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
+// Corrected divisions stay finite while |z| / d <= 2^100; larger quotients
+// (possible only when the global scale comes from another tensor's amax) take
+// true divisions.
+constexpr float kQuotientLimit = 0x1p100f;
+constexpr int64_t kLastLevelKeep = 176LL << 20;  // bytes of input pass 1 leaves cached
+// Arrival counters of the quantize pass when pass 1 leaves its partial maxima
+// in q_out: spread over kCounters words on separate 128-byte lines, since
+// thousands of increments of one word serialize (and a workgroup's loads
+// wait behind its own pending atomic).
+constexpr int kCounters = 64;
+constexpr int kCounterStride = 32;  // words
+__host__ __device__ constexpr int64_t counter_base(int64_t npartials) {
+  return (npartials + kCounterStride - 1) / kCounterStride * kCounterStride;  // words
+}
+__host__ __device__ constexpr int64_t head_bytes(int64_t npartials) {
+  return 4 * (counter_base(npartials) + kCounters * kCounterStride);
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), off, 64)));
+  return u;
+}
+
+// Workgroup maximum, then either one atomicMax per workgroup on a zeroed word
+// (partials == 0), or a plain store of the workgroup's maximum to out[wg]
+// (partials == 1; workgroup 0 also clears the arrival counters the quantize
+// pass uses, so no word has to be zeroed beforehand).  Non-negative binary32
+// values order like their bit patterns, so the maximum is exact and the same
+// for any reduction order (a NaN input stays visible as bits above +inf).
+__device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restrict__ out,
+                                                 int partials) {
+  __shared__ uint32_t part[kThreads / 64];
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = part[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = umax(r, part[i]);
+    if (partials)
+      out[blockIdx.x] = r;
+    else
+      atomicMax(out, r);
+  }
+  if (partials && blockIdx.x == 0 && threadIdx.x < kCounters)
+    out[counter_base(gridDim.x) + threadIdx.x * kCounterStride] = 0u;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+__global__ void zero_word_kernel(uint32_t* __restrict__ w) { *w = 0u; }
+
+// Non-temporal 16-byte loads: data that no later pass will find in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nontemporal(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// One 16-value fp32 block: elements 0..7 into lo, 8..15 into hi.
+__device__ __forceinline__ void load_block(const float* __restrict__ x, int64_t b, float lo[8],
+                                           float hi[8]) {
+  const float4* p = reinterpret_cast<const float4*>(x + b * 16);
+  const float4 a = p[0], c = p[1], d = p[2], e = p[3];
+  lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
+  lo[4] = c.x; lo[5] = c.y; lo[6] = c.z; lo[7] = c.w;
+  hi[0] = d.x; hi[1] = d.y; hi[2] = d.z; hi[3] = d.w;
+  hi[4] = e.x; hi[5] = e.y; hi[6] = e.z; hi[7] = e.w;
+}
+
+// One 16-value bf16 block (32 bytes), widened.
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t b, float lo[8],
+                                           float hi[8]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
+  widen8(p[0], lo);
+  widen8(p[1], hi);
+}
+
+}  // namespace
+}  // namespace nvfp4rq

@@ -1,26 +1,33 @@
-// Fused block-Hadamard rotation + NVFP4 activation quantization for gfx950.
+// Fused block-Hadamard rotation + NVFP4 activation quantization for gfx950:
+// host side and C ABI of libnvfp4rq.  The kernels are in common.hpp (shared
+// constants, reductions, loads), pass1.hpp (rotated amax), pass2.hpp
+// (quantize), mxfp4.hpp (MXFP4 variant) and elementwise.hpp (decode, rotation
+// alone); all are compiled in this one translation unit.
 //
 // Method: page "A Fused Hadamard + NVFP4 Quantization Kernel in Triton"
 // (kanthi.in), sections 1-3; stored layout: page "NVFP4 Quantization"
 // (atlas-docs), section "The numeric format".  The C ABI and its contract are
 // in include/nvfp4rq.h.
 //
-// Two passes over the input:
-//   rotamax   reads every 16-value block, rotates it in registers, and keeps
-//             the running max |y| as binary32 bits (non-negative floats order
-//             like unsigned integers, so the max is exact and independent of
-//             the reduction order); wave and workgroup maxima, then one
-//             atomicMax per workgroup into the caller's amax word.
-//   rotquant  every workgroup derives the global scale from that word, then
-//             each lane loads a block, rotates it, scales and encodes it, and
-//             writes 8 code bytes and 1 scale byte.  The rotated tensor never
-//             leaves registers.
+// The fused call is two kernels:
+//   pass 1  reads every 16-value block, rotates it in registers, and keeps
+//           the running max |y| as binary32 bits (non-negative floats order
+//           like unsigned integers, so the max is exact and independent of
+//           the reduction order); each workgroup stores its maximum at the
+//           head of q_out (or, for small tensors and the pass-level entry
+//           point, does one atomicMax into a zeroed amax word).
+//   pass 2  every workgroup reduces those maxima and derives the global
+//           scale, then each lane loads a block, rotates it, scales and
+//           encodes it, and writes 8 code bytes and 1 scale byte.  The
+//           rotated tensor never leaves registers.
 //
 // Arithmetic: binary32, round to nearest even, denormals kept (gfx950
 // default), no contraction (-ffp-contract=off); the divisions are the
-// compiler's correctly rounded binary32 division.
+// compiler's correctly rounded binary32 division or sequences proven equal
+// to it.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstddef>
 #include <cstdlib>
@@ -29,715 +36,14 @@
 #include <utility>
 
 #include "nvfp4rq.h"
-#include "nvfp4rq_device.hpp"
+#include "common.hpp"
+#include "pass1.hpp"
+#include "pass2.hpp"
+#include "mxfp4.hpp"
+#include "elementwise.hpp"
 
+namespace nvfp4rq {
 namespace {
-
-using namespace nvfp4rq;
-
-constexpr int kThreads = 256;      // 4 waves of 64
-constexpr int kAmaxPieces = 8;     // 16-byte pieces per lane per iteration in the bf16 amax pass
-
-// The fast path (corrected divisions with per-scale reciprocals) is used for
-// bf16 input when the global amax lies in [2^-38, 2^15): then every divisor is
-// in [2^-58.4, 2^14.4] and every quotient stays inside the range on which the
-// corrected division was enumerated.  Other tensors take the exact path
-// (IEEE divisions); both give identical bytes.
-constexpr uint32_t kFastAmaxLo = 0x2C800000u;   // 2^-38
-constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
-// Corrected divisions stay finite while |z| / d <= 2^100; larger quotients
-// (possible only when the global scale comes from another tensor's amax) take
-// true divisions.
-constexpr float kQuotientLimit = 0x1p100f;
-constexpr int64_t kLastLevelKeep = 176LL << 20;  // bytes of input pass 1 leaves cached
-// Arrival counters of the quantize pass when pass 1 leaves its partial maxima
-// in q_out: spread over kCounters words on separate 128-byte lines, since
-// thousands of increments of one word serialize (and a workgroup's loads
-// wait behind its own pending atomic).
-constexpr int kCounters = 64;
-constexpr int kCounterStride = 32;  // words
-__host__ __device__ constexpr int64_t counter_base(int64_t npartials) {
-  return (npartials + kCounterStride - 1) / kCounterStride * kCounterStride;  // words
-}
-__host__ __device__ constexpr int64_t head_bytes(int64_t npartials) {
-  return 4 * (counter_base(npartials) + kCounters * kCounterStride);
-}
-
-// ---------------------------------------------------------------- reductions
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1)
-    u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), off, 64)));
-  return u;
-}
-
-// Workgroup maximum, then either one atomicMax per workgroup on a zeroed word
-// (partials == 0), or a plain store of the workgroup's maximum to out[wg]
-// (partials == 1; workgroup 0 also clears the arrival counters the quantize
-// pass uses, so no word has to be zeroed beforehand).  Non-negative binary32
-// values order like their bit patterns, so the maximum is exact and the same
-// for any reduction order (a NaN input stays visible as bits above +inf).
-__device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restrict__ out,
-                                                 int partials) {
-  __shared__ uint32_t part[kThreads / 64];
-  m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = part[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) r = umax(r, part[i]);
-    if (partials)
-      out[blockIdx.x] = r;
-    else
-      atomicMax(out, r);
-  }
-  if (partials && blockIdx.x == 0 && threadIdx.x < kCounters)
-    out[counter_base(gridDim.x) + threadIdx.x * kCounterStride] = 0u;
-}
-
-__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
-
-// ---------------------------------------------------------------- kernels
-
-__global__ void zero_word_kernel(uint32_t* __restrict__ w) { *w = 0u; }
-
-// Pass 1 for bf16 (section 2: the global scale needs the amax of the whole
-// rotated tensor before any block can be scaled).  Coalesced: in each
-// iteration a wave reads 64 * kAmaxPieces consecutive 16-byte pieces, lane l
-// taking pieces l, l + 64, ...; a piece is half a block, so lanes 2k and 2k+1
-// hold elements 0..7 and 8..15 of one block.  Each lane runs the stride-1, 2,
-// 4 stages on its half; the stride-8 stage pairs the two lanes, and
-// max(|a + b|, |a - b|) = RN(|a| + |b|) exactly (rounding to nearest is
-// symmetric), so one DPP-fed add per element gives the block's largest |z|.
-// Both lanes compute the same sums; the maximum absorbs the duplicate.
-// max |0.25 z| = RN(0.25 max |z|) because rounding is monotone, so the scaling
-// is applied once at the end.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_nontemporal(const uint4* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-template <bool ROTATE>
-__global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                int64_t nb,
-                                                                uint32_t* __restrict__ amax_bits,
-                                                                int partials, int64_t nt_end) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  const int64_t npieces = 2 * nb;
-  constexpr int64_t kPerWave = 64 * kAmaxPieces;
-  const uint4* __restrict__ p = reinterpret_cast<const uint4*>(x);
-  uint32_t m = 0u;
-  for (int64_t base = wave * kPerWave; base < npieces; base += nwaves * kPerWave) {
-    uint4 v[kAmaxPieces];
-    if (base + kPerWave <= nt_end) {       // streamed past the caches (see launch_rotamax)
-#pragma unroll
-      for (int j = 0; j < kAmaxPieces; ++j) v[j] = load_nontemporal(p + base + j * 64 + lane);
-    } else if (base + kPerWave <= npieces) {  // wave-uniform: every piece in range
-#pragma unroll
-      for (int j = 0; j < kAmaxPieces; ++j) v[j] = p[base + j * 64 + lane];
-    } else {                               // the tensor's last, partial chunk
-#pragma unroll
-      for (int j = 0; j < kAmaxPieces; ++j) {
-        const int64_t pc = base + j * 64 + lane;
-        v[j] = pc < npieces ? p[pc] : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kAmaxPieces; ++j) {
-      float z[8];
-      widen8(v[j], z);
-      if (ROTATE) {
-        stages_1_2_4(z);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          m = umax(m, __float_as_uint(__builtin_fabsf(z[i]) + __builtin_fabsf(swap_lane1(z[i]))));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = umax(m, abs_bits(z[i]));
-      }
-    }
-  }
-  if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
-  workgroup_max_to(m, amax_bits, partials);
-}
-
-// One 16-value fp32 block: elements 0..7 into lo, 8..15 into hi.
-__device__ __forceinline__ void load_block(const float* __restrict__ x, int64_t b, float lo[8],
-                                           float hi[8]) {
-  const float4* p = reinterpret_cast<const float4*>(x + b * 16);
-  const float4 a = p[0], c = p[1], d = p[2], e = p[3];
-  lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
-  lo[4] = c.x; lo[5] = c.y; lo[6] = c.z; lo[7] = c.w;
-  hi[0] = d.x; hi[1] = d.y; hi[2] = d.z; hi[3] = d.w;
-  hi[4] = e.x; hi[5] = e.y; hi[6] = e.z; hi[7] = e.w;
-}
-
-// One 16-value bf16 block (32 bytes), widened.
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t b, float lo[8],
-                                           float hi[8]) {
-  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
-  widen8(p[0], lo);
-  widen8(p[1], hi);
-}
-
-// Pass 1 for fp32: one block per lane per iteration.
-template <bool ROTATE>
-__global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __restrict__ x,
-                                                               int64_t nb,
-                                                               uint32_t* __restrict__ amax_bits,
-                                                               int partials) {
-  uint32_t m = 0u;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb; b += stride) {
-    float lo[8], hi[8];
-    load_block(x, b, lo, hi);
-    if (ROTATE) {
-      stages_1_2_4(lo);
-      stages_1_2_4(hi);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        m = umax(m, __float_as_uint(__builtin_fabsf(lo[i]) + __builtin_fabsf(hi[i])));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = umax(umax(m, abs_bits(lo[i])), abs_bits(hi[i]));
-    }
-  }
-  if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
-  workgroup_max_to(m, amax_bits, partials);
-}
-
-// Where block b's scale byte is stored.  Row-major: byte b of the
-// [rows, cols/16] matrix.  Swizzled (the tiled layout GEMMs read, page "A
-// Fused Hadamard + NVFP4 Quantization Kernel in Triton", section 6; layout as
-// the GEMM library documentation it cites defines it for 16-element block
-// scales): the matrix padded to 128-row x 4-column tiles of 512 bytes, tiles
-// stored tile-row by tile-row, and S[128 rt + 32 i + j][4 ct + k] at byte
-// 512 (rt * ctiles + ct) + 16 j + 4 i + k.  Block indices fit in 32 bits
-// (checked on the host).
-// Each policy also fixes which blocks a pass-2 workgroup handles together
-// (a chunk): kSub groups of kThreads blocks.  Row-major: 256 consecutive
-// blocks.  Swizzled: a super-tile of 128 rows x 16 blocks, so that one
-// workgroup writes whole 512-byte scale tiles and whole 128-byte lines of
-// codes (lines completed from several L2s are written back piecemeal).
-struct RowMajorScales {
-  static constexpr int kSub = 1;
-  static constexpr bool kStaged = false;
-  __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
-  __host__ __device__ int64_t chunks(int64_t nb) const { return (nb + kThreads - 1) / kThreads; }
-  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const { return chunk * kThreads * 8; }
-  __device__ __forceinline__ bool locate(int64_t chunk, int, uint32_t tid, int64_t nb, int64_t* b,
-                                         int64_t* si) const {
-    *b = chunk * kThreads + tid;
-    *si = *b;
-    return *b < nb;
-  }
-};
-struct SwizzledScales {
-  static constexpr int kSub = 8;
-  static constexpr bool kStaged = true;  // scale tiles assembled in LDS
-  int64_t rows;
-  uint32_t cb, ctiles, cs;  // blocks per row, ceil(cb / 4), ceil(cb / 16)
-  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const {
-    const int64_t rt = chunk / cs;
-    return (rt * 128 * cb + (chunk - rt * cs) * 16) * 8;
-  }
-  __device__ __forceinline__ static int64_t place(uint32_t r, uint32_t c, uint32_t ctiles) {
-    const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
-    return static_cast<int64_t>(tile * 512u + (((r & 31u) << 4) | (((r >> 5) & 3u) << 2) | (c & 3u)));
-  }
-  __device__ __forceinline__ int64_t operator()(int64_t b) const {
-    const uint32_t bb = static_cast<uint32_t>(b);
-    const uint32_t r = bb / cb;
-    return place(r, bb - r * cb, ctiles);
-  }
-  __host__ __device__ int64_t chunks(int64_t) const { return ((rows + 127) / 128) * cs; }
-  __device__ __forceinline__ bool locate(int64_t chunk, int sub, uint32_t tid, int64_t, int64_t* b,
-                                         int64_t* si) const {
-    const int64_t rt = chunk / cs;
-    const uint32_t r = static_cast<uint32_t>(rt * 128 + sub * 16 + (tid >> 4));
-    const uint32_t c = static_cast<uint32_t>(chunk - rt * cs) * 16 + (tid & 15u);
-    if (r >= rows || c >= cb) return false;
-    *b = static_cast<int64_t>(r) * cb + c;
-    *si = place(r & 127u, c & 15u, 4);  // byte within the chunk's tiles
-    return true;
-  }
-  // The chunk's tiles (rt, 4 c16 .. 4 c16 + 3) are consecutive in memory.
-  __device__ __forceinline__ void chunk_tiles(int64_t chunk, int64_t* first_byte, int* ntiles) const {
-    const int64_t rt = chunk / cs, ct0 = (chunk - rt * cs) * 4;
-    *first_byte = (rt * ctiles + ct0) * 512;
-    *ntiles = static_cast<int>(ctiles - ct0 < 4 ? ctiles - ct0 : 4);
-  }
-};
-
-// When pass 1 leaves its per-workgroup maxima at the head of q_out, every
-// pass-2 workgroup reads them in its prologue and then counts itself in; a
-// workgroup waits for all of them to have done so before it writes a chunk
-// whose codes reach into that head.  Chunks run last-first, so the wait comes
-// at the end of the few workgroups concerned, and since the others never wait
-// the count always completes.  The wait is bounded: past spin_limit sleeps the
-// workgroup goes on and marks the call failed with a NaN global scale.
-struct HeadGuard {
-  uint32_t* counters;  // null: no partials in q_out
-  int64_t bytes;       // head bytes holding partials and counters
-  uint32_t need;       // pass-2 workgroups
-  uint32_t spin_limit;
-  float* gscale_out;
-};
-
-__device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
-  __shared__ int timed_out;
-  if (threadIdx.x < 64) {  // wave 0: one counter per lane
-    uint32_t spins = 0;
-    int late = 0;
-    // Relaxed: acquire/release at agent scope would write back or invalidate
-    // the L2 of every XCD involved on each poll.  Nothing written by other
-    // workgroups is read after the wait; the waiter's stores follow the loop.
-    for (;;) {
-      uint32_t c = __hip_atomic_load(h.counters + threadIdx.x * kCounterStride, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
-      if (c >= h.need) break;
-      if (++spins > h.spin_limit) {
-        late = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    if (threadIdx.x == 0) timed_out = late;
-  }
-  __syncthreads();
-  if (timed_out && threadIdx.x == 0) *h.gscale_out = __uint_as_float(0x7FC00000u);
-}
-
-// Pass 2 body: each lane rotates, scales and encodes one block per iteration.
-// Workgroup w handles the 256-block chunks w, w + G, w + 2G, ... (G = grid
-// size), last chunk first: the chunks pass 1 read last are the likeliest to
-// still be in the last-level cache.  Every step is the definition of section 2
-// (hadamard_nvfp4_kernel) in binary32:
-//   z     = S16 x                         (butterfly, no scaling yet)
-//   a_b   = max |y| = 0.25 max |z|        (exact for any rounding, see pass 1)
-//   v     = (a_b / 6) / g,  s = E4M3(min(v, 448))
-//   d     = float(s) * g, or 1 when that is 0
-//   code  = E2M1(y / d),  y = 0.25 z
-// FAST (bf16 in the guarded range): y / d = z / (4d) exactly (the scalings by
-// 4 are exact there), the divisions are corrected reciprocal products and the
-// per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
-// Otherwise every division is a true binary32 division.
-// A lane's first block, loaded (as raw bits) before the kernel's prologue so
-// that the load latency overlaps the amax reduction and the table set-up.
-template <typename T>
-struct FirstBlock;
-template <>
-struct FirstBlock<uint16_t> {
-  uint4 a, b;
-  __device__ __forceinline__ void load(const uint16_t* x, int64_t blk) {
-    const uint4* p = reinterpret_cast<const uint4*>(x + blk * 16);
-    a = p[0];
-    b = p[1];
-  }
-  __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
-    widen8(a, lo);
-    widen8(b, hi);
-  }
-};
-template <>
-struct FirstBlock<float> {
-  float4 a, b, c, d;
-  __device__ __forceinline__ void load(const float* x, int64_t blk) {
-    const float4* p = reinterpret_cast<const float4*>(x + blk * 16);
-    a = p[0];
-    b = p[1];
-    c = p[2];
-    d = p[3];
-  }
-  __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
-    lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
-    lo[4] = b.x; lo[5] = b.y; lo[6] = b.z; lo[7] = b.w;
-    hi[0] = c.x; hi[1] = c.y; hi[2] = c.z; hi[3] = c.w;
-    hi[4] = d.x; hi[5] = d.y; hi[6] = d.z; hi[7] = d.w;
-  }
-};
-
-template <typename T, typename SMAP>
-__device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, SMAP smap,
-                                           FirstBlock<T>* f) {
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
-  int64_t b, si;
-  if (mine > 0 && smap.locate((mine - 1) * gridDim.x + blockIdx.x, 0, threadIdx.x, nb, &b, &si))
-    f->load(x, b);
-}
-
-template <typename T, bool ROTATE, bool FAST, typename SMAP>
-__device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
-                                             const float2* __restrict__ tab,
-                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                             SMAP smap, const HeadGuard& head,
-                                             const FirstBlock<T>& first) {
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
-  const float rg = FAST ? 1.0f / g : 0.0f;
-  __shared__ uint32_t stage[SMAP::kStaged ? 512 : 1];  // 4 scale tiles
-  for (int64_t it = mine - 1; it >= 0; --it) {
-   const int64_t chunk = it * gridDim.x + blockIdx.x;
-   if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
-   if constexpr (SMAP::kStaged) {
-     for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
-     __syncthreads();
-   }
-#pragma unroll 1
-   for (int sub = 0; sub < SMAP::kSub; ++sub) {
-    int64_t b, si;
-    if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
-    float lo[8], hi[8];
-    if (!SMAP::kStaged && it == mine - 1 && sub == 0) {  // loaded before the prologue
-      first.unpack(lo, hi);
-    } else {
-      load_block(x, b, lo, hi);
-    }
-    if (ROTATE) {
-      stages_1_2_4(lo);
-      stages_1_2_4(hi);
-      stage_8(lo, hi);
-    }
-    float az = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
-    uint32_t sb;
-    if (FAST) {
-      const float ab = ROTATE ? 0.25f * az : az;
-      const float a6 = div_corrected(ab, 6.0f, kRecip6);
-      // A quotient too large for binary32 makes the product NaN; fminf keeps
-      // 448, the right byte for any block value that large.
-      sb = e4m3_byte(div_corrected(a6, g, rg));
-      const float2 t = tab[sb];
-      if (az <= kQuotientLimit * t.x) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lo[i] = div_corrected(lo[i], t.x, t.y);
-          hi[i] = div_corrected(hi[i], t.x, t.y);
-        }
-      } else {
-        // Only with a global scale from elsewhere (the amax of an earlier
-        // step) can a block's quotients approach the binary32 range; divide
-        // exactly (y = z / 4 and d = 4d / 4 are exact here).
-        const float d = ROTATE ? 0.25f * t.x : t.x;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
-          hi[i] = (ROTATE ? 0.25f * hi[i] : hi[i]) / d + 0.0f;
-        }
-      }
-    } else {
-      if (ROTATE) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lo[i] = 0.25f * lo[i];
-          hi[i] = 0.25f * hi[i];
-        }
-      }
-      const float ab = ROTATE ? 0.25f * az : az;
-      sb = e4m3_byte((ab / 6.0f) / g);
-      const float sf = e4m3_value(sb) * g;
-      const float d = sf == 0.0f ? 1.0f : sf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo[i] = lo[i] / d + 0.0f;
-        hi[i] = hi[i] / d + 0.0f;
-      }
-    }
-    *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
-    if constexpr (SMAP::kStaged)
-      reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
-    else
-      s[si] = static_cast<uint8_t>(sb);
-   }
-   if constexpr (SMAP::kStaged) {
-     // whole tiles, padding zeros included, in one coalesced store
-     __syncthreads();
-     int64_t first;
-     int ntiles;
-     smap.chunk_tiles(chunk, &first, &ntiles);
-     uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
-     for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
-       dst[i] = stage[i];
-     __syncthreads();
-   }
-  }
-}
-
-// amax_src: the amax word (npartials == 0) or pass 1's per-workgroup maxima
-// at the head of q (npartials of them, then the counter; amax_out receives
-// their maximum).
-// Eight workgroups per CU (the grid size assumes it): at most 64 VGPRs.
-template <typename T, bool ROTATE, typename SMAP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
-                                                            const uint32_t* amax_src,
-                                                            int npartials, float* __restrict__ amax_out,
-                                                            uint32_t spin_limit, int allow_fast,
-                                                            uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s,
-                                                            float* __restrict__ gscale_out,
-                                                            SMAP smap) {
-  __shared__ float2 tab[128];
-  __shared__ uint32_t red[kThreads / 64];
-  FirstBlock<T> first;
-  if constexpr (!SMAP::kStaged) load_first(x, nb, smap, &first);  // staged: no registers to spare
-  HeadGuard head{nullptr, 0, 0, spin_limit, gscale_out};
-  uint32_t abits;
-  if (npartials == 0) {
-    abits = *amax_src;
-  } else {
-    uint32_t m = 0u;
-    for (int i = threadIdx.x; i < npartials; i += kThreads) m = umax(m, amax_src[i]);
-    m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    abits = red[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) abits = umax(abits, red[i]);
-    uint32_t* counters = const_cast<uint32_t*>(amax_src) + counter_base(npartials);
-    // every thread's read of the partials is complete (their values met at
-    // the barrier) before the workgroup counts itself in; a relaxed increment
-    // needs no cache write-back
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *amax_out = __uint_as_float(abits);
-    head = HeadGuard{counters, head_bytes(npartials), gridDim.x, spin_limit, gscale_out};
-  }
-  const float g = global_scale(__uint_as_float(abits));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
-  if constexpr (sizeof(T) == 2) {
-    // uniform across the grid: every workgroup reads the same amax
-    if (allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
-      if (threadIdx.x < 128) {
-        const float sf = e4m3_value(threadIdx.x) * g;
-        const float d = (ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf);
-        tab[threadIdx.x] = make_float2(d, 1.0f / d);
-      }
-      __syncthreads();
-      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head, first);
-      return;
-    }
-  }
-  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head, first);
-}
-
-// Kernels that write fp32 per element (decode, rotation alone) use a
-// quarter-block layout: a wave takes 64 * kQuarters consecutive 4-element
-// quarters per iteration, lane l quarters l, l + 64, ..., so that every store
-// instruction of the wave writes 1 KiB of consecutive outputs.  A block's four
-// quarters sit in the four lanes of a quad; strides 1 and 2 of the butterfly
-// run in lane, strides 4 and 8 through quad lane exchanges.  The tail
-// iteration is wave-uniform and every lane runs the exchanges; only the loads
-// and stores are predicated.
-constexpr int kQuarters = 8;
-
-__device__ __forceinline__ void load_quarter(const float* __restrict__ x, int64_t pc, float z[4]) {
-  const float4 v = reinterpret_cast<const float4*>(x)[pc];
-  z[0] = v.x; z[1] = v.y; z[2] = v.z; z[3] = v.w;
-}
-
-__device__ __forceinline__ void load_quarter(const uint16_t* __restrict__ x, int64_t pc,
-                                             float z[4]) {
-  const uint2 v = reinterpret_cast<const uint2*>(x)[pc];
-  z[0] = bf16_lo(v.x); z[1] = bf16_hi(v.x); z[2] = bf16_lo(v.y); z[3] = bf16_hi(v.y);
-}
-
-// Dequantize (section 2, dequantize): +-GRID[c & 7] * RN(float(s) * g), then
-// the same butterfly and * 0.25 when rotated (H16 is symmetric, so H16^T is
-// the forward transform).  nq = number of quarters = rows * cols / 4.
-template <typename SMAP>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ q,
-                                                           const uint8_t* __restrict__ s,
-                                                           const float* __restrict__ gscale,
-                                                           int64_t nq, int rotate,
-                                                           float* __restrict__ y, SMAP smap) {
-  const uint32_t lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  constexpr int64_t kPerWave = 64 * kQuarters;
-  const uint16_t* __restrict__ q2 = reinterpret_cast<const uint16_t*>(q);  // 4 codes
-  float4* __restrict__ o = reinterpret_cast<float4*>(y);
-  const float g = *gscale;
-  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
-    uint32_t c[kQuarters], sb[kQuarters];
-#pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      const int64_t pc = base + j * 64 + lane;
-      const bool in = pc < nq;
-      c[j] = in ? q2[pc] : 0u;
-      sb[j] = in ? s[smap(pc >> 2)] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      const float sf = e4m3_value(sb[j]) * g;
-      float z[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = e2m1_value((c[j] >> (4 * i)) & 15u) * sf;
-      if (rotate) {
-        stages_1_2(z);
-        quad_stages_4_8(z, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = 0.25f * z[i];
-      }
-      const int64_t pc = base + j * 64 + lane;
-      if (pc < nq) o[pc] = make_float4(z[0], z[1], z[2], z[3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- rotation alone
-
-// y = x H16 per 16-element block (butterfly, then * 0.25), stored as fp32.
-// The first kernel of the unfused three-kernel arrangement that the page
-// "A Fused Hadamard + NVFP4 Quantization Kernel in Triton" compares the fused
-// kernel against (opening paragraph; "Try this" item 4): rotated values go to
-// HBM and the amax and quantize kernels read them back with rotation off.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void rotate_kernel(const T* __restrict__ x, int64_t nq,
-                                                          float* __restrict__ y) {
-  const uint32_t lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  constexpr int64_t kPerWave = 64 * kQuarters;
-  float4* __restrict__ o = reinterpret_cast<float4*>(y);
-  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
-    float z[kQuarters][4];
-    if (base + kPerWave <= nq) {           // wave-uniform: every quarter in range
-#pragma unroll
-      for (int j = 0; j < kQuarters; ++j) load_quarter(x, base + j * 64 + lane, z[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kQuarters; ++j) {
-        const int64_t pc = base + j * 64 + lane;
-        if (pc < nq) {
-          load_quarter(x, pc, z[j]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[j][i] = 0.0f;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      stages_1_2(z[j]);
-      quad_stages_4_8(z[j], lane);
-      const int64_t pc = base + j * 64 + lane;
-      if (pc < nq)
-        o[pc] = make_float4(0.25f * z[j][0], 0.25f * z[j][1], 0.25f * z[j][2], 0.25f * z[j][3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- MXFP4 variant
-
-// MXFP4 (the contrast format of section 1 of the page: 32-element blocks,
-// power-of-two E8M0 scales; the page "Hopper kernel for MXFP4" stores a scale
-// as a biased exponent byte, value 2^(byte - 127)).  There is no global scale,
-// so this is a single pass: each lane rotates (each 16-element half with H16),
-// scales and encodes one 32-element block per iteration.  Readings: the scale
-// is the smallest power of two at or above fl(block_amax / 6), exponent
-// clamped to [-127, 127], 0 for an all-zero block; v = fl(y / scale), which
-// is the exact product y * 2^-e rounded once; then the E2M1 rule of the NVFP4
-// path (+0.0 turns an underflowed -0.0 into +0.0: code 0, not 8).
-template <typename T, bool ROTATE>
-__global__ __launch_bounds__(kThreads) void mx_quant_kernel(const T* __restrict__ x, int64_t nb32,
-                                                            uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb32; b += stride) {
-    float v[4][8];     // halves: (v[0], v[1]) elements 0..15, (v[2], v[3]) 16..31
-    load_block(x, 2 * b, v[0], v[1]);
-    load_block(x, 2 * b + 1, v[2], v[3]);
-    if (ROTATE) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        stages_1_2_4(v[2 * h]);
-        stages_1_2_4(v[2 * h + 1]);
-        stage_8(v[2 * h], v[2 * h + 1]);
-      }
-    }
-    float az = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) az = __builtin_fmaxf(az, __builtin_fabsf(v[k][i]));
-    const float t = (ROTATE ? 0.25f * az : az) / 6.0f;
-    int e = -127;
-    if (t > 0.0f) {
-      int fe;
-      const float m = frexpf(t, &fe);          // t = m 2^fe, m in [0.5, 1)
-      e = m == 0.5f ? fe - 1 : fe;             // ceil(log2 t)
-      e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    }
-    // bf16: the butterfly output z = 4y is exact and y * 2^-e = z * 2^(-e-2);
-    // fp32 values may round when scaled by 0.25, so they are scaled first.
-    const bool fold = ROTATE && sizeof(T) == 2;
-    const float inv = ldexpf(1.0f, fold ? -e - 2 : -e);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float y = (ROTATE && !fold) ? 0.25f * v[k][i] : v[k][i];
-        v[k][i] = y * inv + 0.0f;
-      }
-    *reinterpret_cast<uint4*>(q + b * 16) =
-        make_uint4(e2m1_pack8(v[0]), e2m1_pack8(v[1]), e2m1_pack8(v[2]), e2m1_pack8(v[3]));
-    s[b] = static_cast<uint8_t>(e + 127);
-  }
-}
-
-// MXFP4 dequantize: +-GRID[c & 7] * 2^(byte - 127), rounded to binary32, then
-// the inverse rotation of each 16-element half (the same butterfly and
-// * 0.25).  Quarter-block layout as for the NVFP4 decode; a 32-element block
-// is two quads.
-__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ q,
-                                                              const uint8_t* __restrict__ s,
-                                                              int64_t nq, int rotate,
-                                                              float* __restrict__ y) {
-  const uint32_t lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  constexpr int64_t kPerWave = 64 * kQuarters;
-  const uint16_t* __restrict__ q2 = reinterpret_cast<const uint16_t*>(q);
-  float4* __restrict__ o = reinterpret_cast<float4*>(y);
-  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
-    uint32_t c[kQuarters], sb[kQuarters];
-#pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      const int64_t pc = base + j * 64 + lane;
-      const bool in = pc < nq;
-      c[j] = in ? q2[pc] : 0u;
-      sb[j] = in ? s[pc >> 3] : 127u;
-    }
-#pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      const float sc = ldexpf(1.0f, static_cast<int>(sb[j]) - 127);
-      float z[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = e2m1_value((c[j] >> (4 * i)) & 15u) * sc;
-      if (rotate) {
-        stages_1_2(z);
-        quad_stages_4_8(z, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = 0.25f * z[i];
-      }
-      const int64_t pc = base + j * 64 + lane;
-      if (pc < nq) o[pc] = make_float4(z[0], z[1], z[2], z[3]);
-    }
-  }
-}
 
 // ---------------------------------------------------------------- host helpers
 
@@ -1068,6 +374,9 @@ nvfp4_status dequant(const uint8_t* q, const uint8_t* s, const float* gscale, in
 }
 
 }  // namespace
+}  // namespace nvfp4rq
+
+using namespace nvfp4rq;
 
 // ---------------------------------------------------------------- C ABI
 

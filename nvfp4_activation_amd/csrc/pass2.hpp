@@ -1,0 +1,337 @@
+// Pass 2: global scale, rotation, block scales and E2M1 codes (page "A Fused
+// Hadamard + NVFP4 Quantization Kernel in Triton", section 2,
+// hadamard_nvfp4_kernel), in row-major or swizzled scale layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "nvfp4rq_device.hpp"
+#include "common.hpp"
+
+namespace nvfp4rq {
+namespace {  // one translation unit (nvfp4rq.hip): internal linkage
+
+// Where block b's scale byte is stored.  Row-major: byte b of the
+// [rows, cols/16] matrix.  Swizzled (the tiled layout GEMMs read, page "A
+// Fused Hadamard + NVFP4 Quantization Kernel in Triton", section 6; layout as
+// the GEMM library documentation it cites defines it for 16-element block
+// scales): the matrix padded to 128-row x 4-column tiles of 512 bytes, tiles
+// stored tile-row by tile-row, and S[128 rt + 32 i + j][4 ct + k] at byte
+// 512 (rt * ctiles + ct) + 16 j + 4 i + k.  Block indices fit in 32 bits
+// (checked on the host).
+// Each policy also fixes which blocks a pass-2 workgroup handles together
+// (a chunk): kSub groups of kThreads blocks.  Row-major: 256 consecutive
+// blocks.  Swizzled: a super-tile of 128 rows x 16 blocks, so that one
+// workgroup writes whole 512-byte scale tiles and whole 128-byte lines of
+// codes (lines completed from several L2s are written back piecemeal).
+struct RowMajorScales {
+  static constexpr int kSub = 1;
+  static constexpr bool kStaged = false;
+  __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
+  __host__ __device__ int64_t chunks(int64_t nb) const { return (nb + kThreads - 1) / kThreads; }
+  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const { return chunk * kThreads * 8; }
+  __device__ __forceinline__ bool locate(int64_t chunk, int, uint32_t tid, int64_t nb, int64_t* b,
+                                         int64_t* si) const {
+    *b = chunk * kThreads + tid;
+    *si = *b;
+    return *b < nb;
+  }
+};
+struct SwizzledScales {
+  static constexpr int kSub = 8;
+  static constexpr bool kStaged = true;  // scale tiles assembled in LDS
+  int64_t rows;
+  uint32_t cb, ctiles, cs;  // blocks per row, ceil(cb / 4), ceil(cb / 16)
+  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const {
+    const int64_t rt = chunk / cs;
+    return (rt * 128 * cb + (chunk - rt * cs) * 16) * 8;
+  }
+  __device__ __forceinline__ static int64_t place(uint32_t r, uint32_t c, uint32_t ctiles) {
+    const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
+    return static_cast<int64_t>(tile * 512u + (((r & 31u) << 4) | (((r >> 5) & 3u) << 2) | (c & 3u)));
+  }
+  __device__ __forceinline__ int64_t operator()(int64_t b) const {
+    const uint32_t bb = static_cast<uint32_t>(b);
+    const uint32_t r = bb / cb;
+    return place(r, bb - r * cb, ctiles);
+  }
+  __host__ __device__ int64_t chunks(int64_t) const { return ((rows + 127) / 128) * cs; }
+  __device__ __forceinline__ bool locate(int64_t chunk, int sub, uint32_t tid, int64_t, int64_t* b,
+                                         int64_t* si) const {
+    const int64_t rt = chunk / cs;
+    const uint32_t r = static_cast<uint32_t>(rt * 128 + sub * 16 + (tid >> 4));
+    const uint32_t c = static_cast<uint32_t>(chunk - rt * cs) * 16 + (tid & 15u);
+    if (r >= rows || c >= cb) return false;
+    *b = static_cast<int64_t>(r) * cb + c;
+    *si = place(r & 127u, c & 15u, 4);  // byte within the chunk's tiles
+    return true;
+  }
+  // The chunk's tiles (rt, 4 c16 .. 4 c16 + 3) are consecutive in memory.
+  __device__ __forceinline__ void chunk_tiles(int64_t chunk, int64_t* first_byte, int* ntiles) const {
+    const int64_t rt = chunk / cs, ct0 = (chunk - rt * cs) * 4;
+    *first_byte = (rt * ctiles + ct0) * 512;
+    *ntiles = static_cast<int>(ctiles - ct0 < 4 ? ctiles - ct0 : 4);
+  }
+};
+
+// When pass 1 leaves its per-workgroup maxima at the head of q_out, every
+// pass-2 workgroup reads them in its prologue and then counts itself in; a
+// workgroup waits for all of them to have done so before it writes a chunk
+// whose codes reach into that head.  Chunks run last-first, so the wait comes
+// at the end of the few workgroups concerned, and since the others never wait
+// the count always completes.  The wait is bounded: past spin_limit sleeps the
+// workgroup goes on and marks the call failed with a NaN global scale.
+struct HeadGuard {
+  uint32_t* counters;  // null: no partials in q_out
+  int64_t bytes;       // head bytes holding partials and counters
+  uint32_t need;       // pass-2 workgroups
+  uint32_t spin_limit;
+  float* gscale_out;
+};
+
+__device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
+  __shared__ int timed_out;
+  if (threadIdx.x < 64) {  // wave 0: one counter per lane
+    uint32_t spins = 0;
+    int late = 0;
+    // Relaxed: acquire/release at agent scope would write back or invalidate
+    // the L2 of every XCD involved on each poll.  Nothing written by other
+    // workgroups is read after the wait; the waiter's stores follow the loop.
+    for (;;) {
+      uint32_t c = __hip_atomic_load(h.counters + threadIdx.x * kCounterStride, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
+      if (c >= h.need) break;
+      if (++spins > h.spin_limit) {
+        late = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (threadIdx.x == 0) timed_out = late;
+  }
+  __syncthreads();
+  if (timed_out && threadIdx.x == 0) *h.gscale_out = __uint_as_float(0x7FC00000u);
+}
+
+// Pass 2 body: each lane rotates, scales and encodes one block per iteration.
+// Workgroup w handles the 256-block chunks w, w + G, w + 2G, ... (G = grid
+// size), last chunk first: the chunks pass 1 read last are the likeliest to
+// still be in the last-level cache.  Every step is the definition of section 2
+// (hadamard_nvfp4_kernel) in binary32:
+//   z     = S16 x                         (butterfly, no scaling yet)
+//   a_b   = max |y| = 0.25 max |z|        (exact for any rounding, see pass 1)
+//   v     = (a_b / 6) / g,  s = E4M3(min(v, 448))
+//   d     = float(s) * g, or 1 when that is 0
+//   code  = E2M1(y / d),  y = 0.25 z
+// FAST (bf16 in the guarded range): y / d = z / (4d) exactly (the scalings by
+// 4 are exact there), the divisions are corrected reciprocal products and the
+// per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
+// Otherwise every division is a true binary32 division.
+// A lane's first block, loaded (as raw bits) before the kernel's prologue so
+// that the load latency overlaps the amax reduction and the table set-up.
+template <typename T>
+struct FirstBlock;
+template <>
+struct FirstBlock<uint16_t> {
+  uint4 a, b;
+  __device__ __forceinline__ void load(const uint16_t* x, int64_t blk) {
+    const uint4* p = reinterpret_cast<const uint4*>(x + blk * 16);
+    a = p[0];
+    b = p[1];
+  }
+  __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
+    widen8(a, lo);
+    widen8(b, hi);
+  }
+};
+template <>
+struct FirstBlock<float> {
+  float4 a, b, c, d;
+  __device__ __forceinline__ void load(const float* x, int64_t blk) {
+    const float4* p = reinterpret_cast<const float4*>(x + blk * 16);
+    a = p[0];
+    b = p[1];
+    c = p[2];
+    d = p[3];
+  }
+  __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
+    lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
+    lo[4] = b.x; lo[5] = b.y; lo[6] = b.z; lo[7] = b.w;
+    hi[0] = c.x; hi[1] = c.y; hi[2] = c.z; hi[3] = c.w;
+    hi[4] = d.x; hi[5] = d.y; hi[6] = d.z; hi[7] = d.w;
+  }
+};
+
+template <typename T, typename SMAP>
+__device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, SMAP smap,
+                                           FirstBlock<T>* f) {
+  const int64_t nchunks = smap.chunks(nb);
+  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  int64_t b, si;
+  if (mine > 0 && smap.locate((mine - 1) * gridDim.x + blockIdx.x, 0, threadIdx.x, nb, &b, &si))
+    f->load(x, b);
+}
+
+template <typename T, bool ROTATE, bool FAST, typename SMAP>
+__device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
+                                             const float2* __restrict__ tab,
+                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                             SMAP smap, const HeadGuard& head,
+                                             const FirstBlock<T>& first) {
+  const int64_t nchunks = smap.chunks(nb);
+  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const float rg = FAST ? 1.0f / g : 0.0f;
+  __shared__ uint32_t stage[SMAP::kStaged ? 512 : 1];  // 4 scale tiles
+  for (int64_t it = mine - 1; it >= 0; --it) {
+   const int64_t chunk = it * gridDim.x + blockIdx.x;
+   if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
+   if constexpr (SMAP::kStaged) {
+     for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
+     __syncthreads();
+   }
+#pragma unroll 1
+   for (int sub = 0; sub < SMAP::kSub; ++sub) {
+    int64_t b, si;
+    if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
+    float lo[8], hi[8];
+    if (!SMAP::kStaged && it == mine - 1 && sub == 0) {  // loaded before the prologue
+      first.unpack(lo, hi);
+    } else {
+      load_block(x, b, lo, hi);
+    }
+    if (ROTATE) {
+      stages_1_2_4(lo);
+      stages_1_2_4(hi);
+      stage_8(lo, hi);
+    }
+    float az = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
+    uint32_t sb;
+    if (FAST) {
+      const float ab = ROTATE ? 0.25f * az : az;
+      const float a6 = div_corrected(ab, 6.0f, kRecip6);
+      // A quotient too large for binary32 makes the product NaN; fminf keeps
+      // 448, the right byte for any block value that large.
+      sb = e4m3_byte(div_corrected(a6, g, rg));
+      const float2 t = tab[sb];
+      if (az <= kQuotientLimit * t.x) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo[i] = div_corrected(lo[i], t.x, t.y);
+          hi[i] = div_corrected(hi[i], t.x, t.y);
+        }
+      } else {
+        // Only with a global scale from elsewhere (the amax of an earlier
+        // step) can a block's quotients approach the binary32 range; divide
+        // exactly (y = z / 4 and d = 4d / 4 are exact here).
+        const float d = ROTATE ? 0.25f * t.x : t.x;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
+          hi[i] = (ROTATE ? 0.25f * hi[i] : hi[i]) / d + 0.0f;
+        }
+      }
+    } else {
+      if (ROTATE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo[i] = 0.25f * lo[i];
+          hi[i] = 0.25f * hi[i];
+        }
+      }
+      const float ab = ROTATE ? 0.25f * az : az;
+      sb = e4m3_byte((ab / 6.0f) / g);
+      const float sf = e4m3_value(sb) * g;
+      const float d = sf == 0.0f ? 1.0f : sf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = lo[i] / d + 0.0f;
+        hi[i] = hi[i] / d + 0.0f;
+      }
+    }
+    *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
+    if constexpr (SMAP::kStaged)
+      reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
+    else
+      s[si] = static_cast<uint8_t>(sb);
+   }
+   if constexpr (SMAP::kStaged) {
+     // whole tiles, padding zeros included, in one coalesced store
+     __syncthreads();
+     int64_t first;
+     int ntiles;
+     smap.chunk_tiles(chunk, &first, &ntiles);
+     uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
+     for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
+       dst[i] = stage[i];
+     __syncthreads();
+   }
+  }
+}
+
+// amax_src: the amax word (npartials == 0) or pass 1's per-workgroup maxima
+// at the head of q (npartials of them, then the counter; amax_out receives
+// their maximum).
+// Eight workgroups per CU (the grid size assumes it): at most 64 VGPRs.
+template <typename T, bool ROTATE, typename SMAP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
+                                                            const uint32_t* amax_src,
+                                                            int npartials, float* __restrict__ amax_out,
+                                                            uint32_t spin_limit, int allow_fast,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ s,
+                                                            float* __restrict__ gscale_out,
+                                                            SMAP smap) {
+  __shared__ float2 tab[128];
+  __shared__ uint32_t red[kThreads / 64];
+  FirstBlock<T> first;
+  if constexpr (!SMAP::kStaged) load_first(x, nb, smap, &first);  // staged: no registers to spare
+  HeadGuard head{nullptr, 0, 0, spin_limit, gscale_out};
+  uint32_t abits;
+  if (npartials == 0) {
+    abits = *amax_src;
+  } else {
+    uint32_t m = 0u;
+    for (int i = threadIdx.x; i < npartials; i += kThreads) m = umax(m, amax_src[i]);
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    abits = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) abits = umax(abits, red[i]);
+    uint32_t* counters = const_cast<uint32_t*>(amax_src) + counter_base(npartials);
+    // every thread's read of the partials is complete (their values met at
+    // the barrier) before the workgroup counts itself in; a relaxed increment
+    // needs no cache write-back
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *amax_out = __uint_as_float(abits);
+    head = HeadGuard{counters, head_bytes(npartials), gridDim.x, spin_limit, gscale_out};
+  }
+  const float g = global_scale(__uint_as_float(abits));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
+  if constexpr (sizeof(T) == 2) {
+    // uniform across the grid: every workgroup reads the same amax
+    if (allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
+      if (threadIdx.x < 128) {
+        const float sf = e4m3_value(threadIdx.x) * g;
+        const float d = (ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf);
+        tab[threadIdx.x] = make_float2(d, 1.0f / d);
+      }
+      __syncthreads();
+      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head, first);
+      return;
+    }
+  }
+  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head, first);
+}
+
+}  // namespace
+}  // namespace nvfp4rq

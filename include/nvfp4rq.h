@@ -42,8 +42,9 @@
  *     may already be enqueued.  Faults inside kernels surface at the caller's
  *     next synchronisation, as usual for HIP.
  *   - Outputs must not overlap the input or each other (NVFP4_ERR_ARG).
- *   - Calls that share an amax/gscale buffer must be ordered (same stream or
- *     explicit events): the amax buffer is an atomic accumulator.
+ *   - Calls that share an output buffer must be ordered (same stream or
+ *     explicit events): the amax word can be an atomic accumulator, and the
+ *     fused call keeps pass 1's partial maxima at the head of q_out.
  *   - No C++ exception crosses this interface.
  */
 #ifndef NVFP4RQ_H

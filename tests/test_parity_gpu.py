@@ -520,3 +520,36 @@ def test_timed_entry_point(nv):
         for k in range(nk):
             ms = ev[2 * k].elapsed_time(ev[2 * k + 1])
             assert 0.0 < ms < 100.0, (k, ms)
+
+
+# ---------------------------------------------------------------- beyond 2^31 elements
+
+def test_beyond_two_to_the_31_elements(nv):
+    """65536 x 32800 bf16 (2.15e9 elements, 4.3 GB): every index past 2^31
+    must be formed in 64 bits.  The tensor repeats one 4096-row block of the
+    Student-t recipe 16 times, with its last 64 rows drawn separately and the
+    largest value in the last row, so the amax and the final blocks depend on
+    data past 2^31; the fused call, the swizzled scales and MXFP4 all match the
+    oracle byte for byte."""
+    rows, cols = 65536, 32800
+    assert rows * cols > 2 ** 31
+    say("[max size] generating")
+    x = np.tile(synth.t3_lognormal(4096, cols, seed=17), (rows // 4096, 1))
+    x[-64:] = synth.t3_lognormal(64, cols, seed=18)
+    x[-1, -7] = synth.round_bf16(np.array([3.0e6]))[0]
+    say("[max size] gpu")
+    xd = to_dev(x)
+    got = [t.cpu() for t in nv.rotquant(xd)]
+    sw = nv.rotquant_swizzled(xd)[1].cpu().numpy()
+    mq, ms = [t.cpu().numpy() for t in nv.mx_rotquant(xd)]
+    torch.cuda.synchronize()
+    del xd
+    say("[max size] oracle")
+    ref = oracle.quantize(x, True)
+    assert float(ref[3]) >= 0.24 * 3.0e6          # the planted value (bf16: 2998272) sets it
+    compare("65536x32800", x, True, got, ref)
+    assert np.array_equal(sw, oracle.swizzle_scales(ref[1]))
+    del sw, got, ref
+    oq, os_ = oracle.mx_quantize(x, True)
+    assert np.array_equal(ms, os_) and np.array_equal(mq, oq)
+    say("[max size] ok")

@@ -553,3 +553,37 @@ def test_beyond_two_to_the_31_elements(nv):
     oq, os_ = oracle.mx_quantize(x, True)
     assert np.array_equal(ms, os_) and np.array_equal(mq, oq)
     say("[max size] ok")
+
+
+# ---------------------------------------------------------------- graph capture
+
+def test_graph_capture_replays(nv):
+    """The fused call captured in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed several times, with new input copied in and eager library calls
+    in between: every replay gives the eager call's bytes for that input (the
+    call allocates nothing and records no memset, so it can be captured)."""
+    rows, cols = 2048, 4096
+    inputs = [mixed_input(rows, cols, "bf16", seed=100 + i) for i in range(4)]
+    xd = to_dev(inputs[0])
+    out = (torch.empty(rows, cols // 2, dtype=torch.uint8, device="cuda:0"),
+           torch.empty(rows, cols // 16, dtype=torch.uint8, device="cuda:0"),
+           torch.empty(1, dtype=torch.float32, device="cuda:0"),
+           torch.empty(1, dtype=torch.float32, device="cuda:0"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        nv.rotquant(xd, out=out)              # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.rotquant(xd, out=out)
+    for i, x in enumerate(inputs[1:] + inputs[:1]):
+        xd.copy_(to_dev(x))
+        eager = [t.clone() for t in nv.rotquant(xd)]   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(out, eager):
+            assert torch.equal(a, b), i
+        compare(f"replay {i}", x, True, out)

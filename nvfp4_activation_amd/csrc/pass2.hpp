@@ -117,20 +117,6 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
   if (timed_out && threadIdx.x == 0) *h.gscale_out = __uint_as_float(0x7FC00000u);
 }
 
-// Pass 2 body: each lane rotates, scales and encodes one block per iteration.
-// Workgroup w handles the 256-block chunks w, w + G, w + 2G, ... (G = grid
-// size), last chunk first: the chunks pass 1 read last are the likeliest to
-// still be in the last-level cache.  Every step is the definition of section 2
-// (hadamard_nvfp4_kernel) in binary32:
-//   z     = S16 x                         (butterfly, no scaling yet)
-//   a_b   = max |y| = 0.25 max |z|        (exact for any rounding, see pass 1)
-//   v     = (a_b / 6) / g,  s = E4M3(min(v, 448))
-//   d     = float(s) * g, or 1 when that is 0
-//   code  = E2M1(y / d),  y = 0.25 z
-// FAST (bf16 in the guarded range): y / d = z / (4d) exactly (the scalings by
-// 4 are exact there), the divisions are corrected reciprocal products and the
-// per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
-// Otherwise every division is a true binary32 division.
 // A lane's first block, loaded (as raw bits) before the kernel's prologue so
 // that the load latency overlaps the amax reduction and the table set-up.
 template <typename T>
@@ -176,6 +162,20 @@ __device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, 
     f->load(x, b);
 }
 
+// Pass 2 body: each lane rotates, scales and encodes one block per iteration.
+// Workgroup w handles the chunks w, w + G, w + 2G, ... of its scale-layout
+// policy (G = grid size), last chunk first: the chunks pass 1 read last are
+// the likeliest to still be in the last-level cache.  Every step is the definition of section 2
+// (hadamard_nvfp4_kernel) in binary32:
+//   z     = S16 x                         (butterfly, no scaling yet)
+//   a_b   = max |y| = 0.25 max |z|        (exact for any rounding, see pass 1)
+//   v     = (a_b / 6) / g,  s = E4M3(min(v, 448))
+//   d     = float(s) * g, or 1 when that is 0
+//   code  = E2M1(y / d),  y = 0.25 z
+// FAST (bf16 in the guarded range): y / d = z / (4d) exactly (the scalings by
+// 4 are exact there), the divisions are corrected reciprocal products and the
+// per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
+// Otherwise every division is a true binary32 division.
 template <typename T, bool ROTATE, bool FAST, typename SMAP>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
                                              const float2* __restrict__ tab,
@@ -187,107 +187,103 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
   const float rg = FAST ? 1.0f / g : 0.0f;
   __shared__ uint32_t stage[SMAP::kStaged ? 512 : 1];  // 4 scale tiles
   for (int64_t it = mine - 1; it >= 0; --it) {
-   const int64_t chunk = it * gridDim.x + blockIdx.x;
-   if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
-   if constexpr (SMAP::kStaged) {
-     for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
-     __syncthreads();
-   }
+    const int64_t chunk = it * gridDim.x + blockIdx.x;
+    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
+    if constexpr (SMAP::kStaged) {
+      for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
+      __syncthreads();
+    }
 #pragma unroll 1
-   for (int sub = 0; sub < SMAP::kSub; ++sub) {
-    int64_t b, si;
-    if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
-    float lo[8], hi[8];
-    if (!SMAP::kStaged && it == mine - 1 && sub == 0) {  // loaded before the prologue
-      first.unpack(lo, hi);
-    } else {
-      load_block(x, b, lo, hi);
-    }
-    if (ROTATE) {
-      stages_1_2_4(lo);
-      stages_1_2_4(hi);
-      stage_8(lo, hi);
-    }
-    float az = 0.0f;
+    for (int sub = 0; sub < SMAP::kSub; ++sub) {
+      int64_t b, si;
+      if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
+      float lo[8], hi[8];
+      if (!SMAP::kStaged && it == mine - 1 && sub == 0) {  // loaded before the prologue
+        first.unpack(lo, hi);
+      } else {
+        load_block(x, b, lo, hi);
+      }
+      if (ROTATE) {
+        stages_1_2_4(lo);
+        stages_1_2_4(hi);
+        stage_8(lo, hi);
+      }
+      float az = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
-    uint32_t sb;
-    if (FAST) {
-      const float ab = ROTATE ? 0.25f * az : az;
-      const float a6 = div_corrected(ab, 6.0f, kRecip6);
-      // A quotient too large for binary32 makes the product NaN; fminf keeps
-      // 448, the right byte for any block value that large.
-      sb = e4m3_byte(div_corrected(a6, g, rg));
-      const float2 t = tab[sb];
-      if (az <= kQuotientLimit * t.x) {
+      for (int i = 0; i < 8; ++i)
+        az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
+      uint32_t sb;
+      if (FAST) {
+        const float ab = ROTATE ? 0.25f * az : az;
+        const float a6 = div_corrected(ab, 6.0f, kRecip6);
+        // A quotient too large for binary32 makes the product NaN; fminf keeps
+        // 448, the right byte for any block value that large.
+        sb = e4m3_byte(div_corrected(a6, g, rg));
+        const float2 t = tab[sb];
+        if (az <= kQuotientLimit * t.x) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lo[i] = div_corrected(lo[i], t.x, t.y);
-          hi[i] = div_corrected(hi[i], t.x, t.y);
+          for (int i = 0; i < 8; ++i) {
+            lo[i] = div_corrected(lo[i], t.x, t.y);
+            hi[i] = div_corrected(hi[i], t.x, t.y);
+          }
+        } else {
+          // Only with a global scale from elsewhere (the amax of an earlier
+          // step) can a block's quotients approach the binary32 range; divide
+          // exactly (y = z / 4 and d = 4d / 4 are exact here).
+          const float d = ROTATE ? 0.25f * t.x : t.x;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
+            hi[i] = (ROTATE ? 0.25f * hi[i] : hi[i]) / d + 0.0f;
+          }
         }
       } else {
-        // Only with a global scale from elsewhere (the amax of an earlier
-        // step) can a block's quotients approach the binary32 range; divide
-        // exactly (y = z / 4 and d = 4d / 4 are exact here).
-        const float d = ROTATE ? 0.25f * t.x : t.x;
+        if (ROTATE) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            lo[i] = 0.25f * lo[i];
+            hi[i] = 0.25f * hi[i];
+          }
+        }
+        const float ab = ROTATE ? 0.25f * az : az;
+        sb = e4m3_byte((ab / 6.0f) / g);
+        const float sf = e4m3_value(sb) * g;
+        const float d = sf == 0.0f ? 1.0f : sf;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
-          hi[i] = (ROTATE ? 0.25f * hi[i] : hi[i]) / d + 0.0f;
+          lo[i] = lo[i] / d + 0.0f;
+          hi[i] = hi[i] / d + 0.0f;
         }
       }
-    } else {
-      if (ROTATE) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lo[i] = 0.25f * lo[i];
-          hi[i] = 0.25f * hi[i];
-        }
-      }
-      const float ab = ROTATE ? 0.25f * az : az;
-      sb = e4m3_byte((ab / 6.0f) / g);
-      const float sf = e4m3_value(sb) * g;
-      const float d = sf == 0.0f ? 1.0f : sf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo[i] = lo[i] / d + 0.0f;
-        hi[i] = hi[i] / d + 0.0f;
-      }
+      *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
+      if constexpr (SMAP::kStaged)
+        reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
+      else
+        s[si] = static_cast<uint8_t>(sb);
     }
-    *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
-    if constexpr (SMAP::kStaged)
-      reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
-    else
-      s[si] = static_cast<uint8_t>(sb);
-   }
-   if constexpr (SMAP::kStaged) {
-     // whole tiles, padding zeros included, in one coalesced store
-     __syncthreads();
-     int64_t first;
-     int ntiles;
-     smap.chunk_tiles(chunk, &first, &ntiles);
-     uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
-     for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
-       dst[i] = stage[i];
-     __syncthreads();
-   }
+    if constexpr (SMAP::kStaged) {
+      // whole tiles, padding zeros included, in one coalesced store
+      __syncthreads();
+      int64_t first;
+      int ntiles;
+      smap.chunk_tiles(chunk, &first, &ntiles);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
+      for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
+        dst[i] = stage[i];
+      __syncthreads();
+    }
   }
 }
 
 // amax_src: the amax word (npartials == 0) or pass 1's per-workgroup maxima
-// at the head of q (npartials of them, then the counter; amax_out receives
-// their maximum).
+// at the head of q (npartials of them, then the arrival counters; amax_out
+// receives their maximum).
 // Eight workgroups per CU (the grid size assumes it): at most 64 VGPRs.
 template <typename T, bool ROTATE, typename SMAP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(const T* __restrict__ x, int64_t nb,
-                                                            const uint32_t* amax_src,
-                                                            int npartials, float* __restrict__ amax_out,
-                                                            uint32_t spin_limit, int allow_fast,
-                                                            uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s,
-                                                            float* __restrict__ gscale_out,
-                                                            SMAP smap) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(
+    const T* __restrict__ x, int64_t nb, const uint32_t* amax_src, int npartials,
+    float* __restrict__ amax_out, uint32_t spin_limit, int allow_fast, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ s, float* __restrict__ gscale_out, SMAP smap) {
   __shared__ float2 tab[128];
   __shared__ uint32_t red[kThreads / 64];
   FirstBlock<T> first;

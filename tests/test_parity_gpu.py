@@ -587,3 +587,36 @@ def test_graph_capture_replays(nv):
         for a, b in zip(out, eager):
             assert torch.equal(a, b), i
         compare(f"replay {i}", x, True, out)
+
+
+# ---------------------------------------------------------------- full-size given-scale and decode
+
+def test_given_scale_and_decode_at_bench_size(nv):
+    """At 16384 x 8192, as the bench times them: the given-scale single pass
+    with an amax kept from another tensor (codes and scales equal to the
+    oracle's), and the decode of the fused call's output (round-trip error
+    within 1e-6 relative of the oracle's fp64 one, every element within 1e-6
+    of its block's largest decoded value)."""
+    w = synth.make("t3_lognormal_16384x8192", rotate=True)
+    xd = to_dev(w.x)
+    other = synth.make("t3_lognormal_16384x8192", rotate=True, seed=9, rows=4096)
+    kept = np.float32(oracle.amax(other.x, True))
+    a = torch.tensor([kept], dtype=torch.float32, device="cuda:0")
+    q, s, g = nv.quant_from_amax(xd, a, rotate=True)
+    torch.cuda.synchronize()
+    og = oracle.global_scale(kept)
+    oq, os_ = oracle.quantize_given_scale(w.x, True, og)
+    compare("given scale 16384x8192", w.x, True, (q, s, g, a), (oq, os_, og, kept))
+    del q, s, oq, os_
+    q, s, g, amax = nv.rotquant(xd, rotate=True)
+    y = nv.dequant(q, s, g, rotate=True)
+    torch.cuda.synchronize()
+    xf = xd.double()
+    e_gpu = ((y.double() - xf).norm() / xf.norm()).item()
+    del xf
+    qn, sn, gn = q.cpu().numpy(), s.cpu().numpy(), float(g.cpu()[0])
+    e_ora = oracle.roundtrip_error(w.x, True, qn, sn, gn)
+    assert abs(e_gpu - e_ora) <= 1e-6 * e_ora, (e_gpu, e_ora)
+    yd = oracle.dequant_f64(qn, sn, gn, True)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - yd).reshape(-1, 16)
+    assert np.all(err <= 1e-6 * np.abs(yd).reshape(-1, 16).max(1, keepdims=True))

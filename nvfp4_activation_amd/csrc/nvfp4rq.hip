@@ -33,6 +33,7 @@
 #include <cstdlib>
 #include <cstdint>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "nvfp4rq.h"
@@ -223,6 +224,10 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const uint32_t* a
                            int npartials, float* amax_out, uint8_t* q, uint8_t* s, float* g,
                            hipStream_t st, SMAP smap = SMAP{}) {
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
+  // bf16: visit chunks on the XCD whose L2 pass 1 left them in (see
+  // RowMajorScales::order); fp32's pass 1 already reads chunk c on XCD c % 8.
+  if constexpr (std::is_same_v<SMAP, RowMajorScales> && sizeof(T) == 2)
+    smap.xcd_order = smap.chunks(nb) % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
   const int64_t spin_env = env_int("NVFP4RQ_SPIN_LIMIT");
   const uint32_t spin_limit = spin_env > 0 ? static_cast<uint32_t>(spin_env) : (1u << 26);
   const dim3 grid(quant_grid(smap.chunks(nb) * kThreads));

@@ -18,8 +18,8 @@ whose two kernels record HIP events at their own start and end: their
 intervals are the live durations of pass 1 and of pass 2 (the dominant
 kernel, used for the roofline figure).
 
-Prints one JSON line (rank 0).  `--gpus N` with N > 1 exits: this build runs
-on one GPU.
+Prints one JSON line (rank 0).  `--gpus N` with N > 1 exits: the benchmark
+measures one GPU.
 """
 from __future__ import annotations
 
@@ -116,9 +116,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true", help="also time graph replay (context)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path "
-              "shards by rows with one 4-byte max exchange, which this build does not run.",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "would shard by rows with one 4-byte max exchange, which this library does not "
+              "implement.", file=sys.stderr)
         return 2
 
     import numpy as np

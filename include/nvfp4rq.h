@@ -110,8 +110,8 @@ nvfp4_status nvfp4_rotquant_f32(const float *x, int64_t rows, int64_t cols, int 
 /*
  * Pass 1 alone: *amax_out = max |y| over the whole tensor, y the rotated
  * blocks (or the values themselves when rotate == 0).  Section 2 of the same
- * page: the global scale needs the amax of the whole rotated tensor before any
- * block can be scaled.  Arguments as nvfp4_rotquant.  The buffer is zeroed and
+ * page: no block scale can be set until the global scale, and with it the
+ * tensor-wide maximum, is known.  Arguments as nvfp4_rotquant.  The buffer is zeroed and
  * then accumulated with one atomic maximum per workgroup.
  */
 nvfp4_status nvfp4_rotamax(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,

@@ -1,6 +1,6 @@
 // Pass 1: the rotated global amax (page "A Fused Hadamard + NVFP4
-// Quantization Kernel in Triton", section 2: the global scale needs the amax
-// of the whole rotated tensor before any block can be scaled).
+// Quantization Kernel in Triton", section 2: every block scale depends on the
+// global scale, hence on the maximum over the entire rotated tensor).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,8 +13,7 @@
 namespace nvfp4rq {
 namespace {  // one translation unit (nvfp4rq.hip): internal linkage
 
-// Pass 1 for bf16 (section 2: the global scale needs the amax of the whole
-// rotated tensor before any block can be scaled).  Coalesced: in each
+// Pass 1 for bf16.  Coalesced: in each
 // iteration a wave reads 64 * kAmaxPieces consecutive 16-byte pieces, lane l
 // taking pieces l, l + 64, ...; a piece is half a block, so lanes 2k and 2k+1
 // hold elements 0..7 and 8..15 of one block.  Each lane runs the stride-1, 2,

@@ -203,8 +203,8 @@ static void block_values(const void *x, int is_f32, int rotate, int64_t b, float
 
 /*
  * Pass 1: the largest |y| over the whole (rotated) tensor (section 2, quantize:
- * the global amax is taken from the rotated tensor before any block can be
- * scaled).  Block b covers elements 16b .. 16b+15 of the row-major tensor,
+ * the wrapper takes this maximum first, since every block scale depends on
+ * it).  Block b covers elements 16b .. 16b+15 of the row-major tensor,
  * which is a reshape to [-1, 16]; with cols % 16 == 0 no block crosses a row.
  */
 float oracle_amax(const void *x, int is_f32, int64_t rows, int64_t cols, int rotate,

@@ -1,7 +1,8 @@
 """Benchmark: rotate + NVFP4-quantize throughput on one MI355X.
 
-Workload: a 16384 x 8192 bf16 activation tensor, Student-t (3 d.o.f.) values
-times per-column log-normal gains, rotation on (seeded synthetic data).
+Workload (default): a 16384 x 8192 bf16 activation tensor, Student-t (3 d.o.f.)
+values times per-column log-normal gains, rotation on (seeded synthetic data).
+`--workload NAME` runs another of the synthetic workloads the same way.
 
 One step = the whole hot path over the tensor, one call of the fused entry
 point: pass 1 (rotated global amax: reads 2 B per element), pass 2 (global
@@ -35,8 +36,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-WORKLOAD = "t3_lognormal_16384x8192"
-ROWS, COLS = 16384, 8192
+DEFAULT_WORKLOAD = "t3_lognormal_16384x8192"
+VALUES = {  # value recipes (seed 0), as the synthetic generators draw them
+    "gauss_outliers_128x1024": "N(0,1), 4 columns x50",
+    "gauss_1pct_cols_4096x4096": "N(0,1), 1% of columns x U(10,100)",
+    "t3_lognormal_16384x8192": "student-t(3) x per-column lognormal(0,1) gain, seed 0",
+    "silu_ties_32768x14336": "SiLU(N(0,1)) x N(0,1), planted exact-midpoint blocks",
+    "kv_heads_65536x8x128_f32": "N(0,1) x per-head U(0.1,10), planted zero and 448-scale blocks",
+}
 
 
 def algorithmic_bytes(n_elem: int, in_bytes: int) -> dict:
@@ -69,7 +76,7 @@ def load_traffic(n_elem: int):
     return d.get("pass2_hbm_bytes")
 
 
-def cpu_baseline(x_np, rotate: bool) -> dict:
+def cpu_baseline(x_np, rotate: bool, label: str) -> dict:
     """The oracle, untuned, on this host's cores: both passes over the whole
     tensor, repeated for about ten seconds (at least three runs), median run.
     A single-thread run on the first 1024 rows is reported beside it."""
@@ -90,17 +97,18 @@ def cpu_baseline(x_np, rotate: bool) -> dict:
             break
     t = statistics.median(times)
     n = x_np.size
-    b = algorithmic_bytes(n, 2)["step"]
+    eb = x_np.dtype.itemsize
+    b = algorithmic_bytes(n, eb)["step"]
     sub = np.ascontiguousarray(x_np[:1024])
     t1 = []
     for _ in range(3):
         t0 = time.perf_counter()
         oracle.quantize(sub, rotate, nthreads=1)
         t1.append(time.perf_counter() - t0)
-    b1 = algorithmic_bytes(sub.size, 2)["step"]
+    b1 = algorithmic_bytes(sub.size, eb)["step"]
     return {"value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": nthreads,
             "kind": "oracle",
-            "sample": f"whole {ROWS}x{COLS} bf16 tensor, both passes, {len(times)} runs in "
+            "sample": f"whole {label} tensor, both passes, {len(times)} runs in "
                       f"{time.perf_counter() - t_start:.1f} s, median {t:.4f} s per run",
             "single_thread_gbs": round(b1 / statistics.median(t1) / 1e9, 4),
             "single_thread_sample": "first 1024 rows, both passes, median of 3"}
@@ -114,6 +122,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="warm-cache timing (context only)")
     ap.add_argument("--graph", action="store_true", help="also time graph replay (context)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="synthetic workload (synth.WORKLOADS); the default is the headline one")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
@@ -133,10 +143,21 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    w = synth.make(WORKLOAD, rotate=True)
-    x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    if args.workload not in synth.WORKLOADS:
+        print(f"unknown workload {args.workload}; one of {sorted(synth.WORKLOADS)}", file=sys.stderr)
+        return 2
+    WORKLOAD = args.workload
+    ROWS, COLS = synth.WORKLOADS[WORKLOAD][:2]
+    ROTATE = True in synth.WORKLOADS[WORKLOAD][3]
+    w = synth.make(WORKLOAD, rotate=ROTATE)
+    if w.x.dtype == np.uint16:
+        x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        dname = "bf16"
+    else:
+        x = torch.from_numpy(w.x).to(dev)
+        dname = "f32"
     n = x.numel()
-    nbytes = algorithmic_bytes(n, 2)
+    nbytes = algorithmic_bytes(n, x.element_size())
     q = torch.empty(ROWS, COLS // 2, dtype=torch.uint8, device=dev)
     s = torch.empty(ROWS, COLS // 16, dtype=torch.uint8, device=dev)
     g = torch.empty(1, dtype=torch.float32, device=dev)
@@ -156,7 +177,7 @@ def main() -> int:
     for _ in range(args.warmup):
         if not args.no_flush:
             cold()
-        nv.rotquant(x, rotate=True, out=out4)
+        nv.rotquant(x, rotate=ROTATE, out=out4)
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, each one call of the fused entry point
@@ -169,7 +190,7 @@ def main() -> int:
         if not args.no_flush:
             cold()
         starts[i].record()
-        nv.rotquant(x, rotate=True, out=out4)
+        nv.rotquant(x, rotate=ROTATE, out=out4)
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -184,12 +205,12 @@ def main() -> int:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            nv.rotquant(x, rotate=True, out=out4)
+            nv.rotquant(x, rotate=ROTATE, out=out4)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            nv.rotquant(x, rotate=True, out=out4)
+            nv.rotquant(x, rotate=ROTATE, out=out4)
         torch.cuda.synchronize()
         gts = []
         for i in range(args.steps):
@@ -202,7 +223,7 @@ def main() -> int:
             gts.append((e0, e1))
         torch.cuda.synchronize()
         graph_ms = statistics.mean(u.elapsed_time(v) for u, v in gts)
-        q3, s3, g3, a3 = nv.rotquant(x, rotate=True)
+        q3, s3, g3, a3 = nv.rotquant(x, rotate=ROTATE)
         torch.cuda.synchronize()
         assert torch.equal(q3, q) and torch.equal(s3, s), "graph replay changed the output"
 
@@ -222,7 +243,7 @@ def main() -> int:
         if not args.no_flush:
             cold()
         outer[i][0].record()
-        *_, nkern = nv.rotquant_timed(x, kev[i], rotate=True, out=out4)
+        *_, nkern = nv.rotquant_timed(x, kev[i], rotate=ROTATE, out=out4)
         outer[i][1].record()
     torch.cuda.synchronize()
     assert nkern == 2, "the fused call takes the two-kernel path at this size"
@@ -239,9 +260,9 @@ def main() -> int:
         e1, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if not args.no_flush:
             cold()
-        nv.rotamax(x, rotate=True, amax=a)
+        nv.rotamax(x, rotate=ROTATE, amax=a)
         e1.record()
-        nv.quant_from_amax(x, a, rotate=True, out=(q, s, g))
+        nv.quant_from_amax(x, a, rotate=ROTATE, out=(q, s, g))
         e2.record()
         gs_ms.append((e1, e2))
     torch.cuda.synchronize()
@@ -266,8 +287,9 @@ def main() -> int:
     # scale): reads 2 B and writes 0.5 + 1/32 B per element.
     qm = torch.empty(ROWS, COLS // 2, dtype=torch.uint8, device=dev)
     sm = torch.empty(ROWS, COLS // 32, dtype=torch.uint8, device=dev)
-    mx_ms = timed(lambda: nv.mx_rotquant(x, rotate=True, out=(qm, sm)))
-    mx_bytes = 2 * n + n // 2 + n // 32
+    mx_ms = timed(lambda: nv.mx_rotquant(x, rotate=ROTATE, out=(qm, sm)))
+    eb = x.element_size()
+    mx_bytes = eb * n + n // 2 + n // 32
 
     # Context: the unfused three-kernel arrangement (rotate to fp32 in HBM,
     # amax over it, quantize it with rotation off); same output bytes.
@@ -282,28 +304,28 @@ def main() -> int:
         nv.rotamax(y32, rotate=False, amax=au)
         nv.quant_from_amax(y32, au, rotate=False, out=(qu, su, gu))
     unfused_ms = timed(unfused)
-    unfused_bytes = 2 * n + 4 * n + 4 * n + 4 * n + n // 2 + n // 16 + 8
+    unfused_bytes = eb * n + 4 * n + 4 * n + 4 * n + n // 2 + n // 16 + 8
     unfused_same = bool(torch.equal(qu, q) and torch.equal(su, s) and torch.equal(gu, g))
 
     # Context: the same step writing the block scales in the 128 x 4-tile
     # swizzled layout (same bytes moved; only the scale-store addresses differ).
     sw = torch.empty(nv.swizzled_scale_bytes(ROWS, COLS), dtype=torch.uint8, device=dev)
-    sw_ms = timed(lambda: nv.rotquant_swizzled(x, rotate=True, out=(qu, sw, gu, au)))
+    sw_ms = timed(lambda: nv.rotquant_swizzled(x, rotate=ROTATE, out=(qu, sw, gu, au)))
 
     # Context: decode (codes + scales + g in, fp32 out, inverse rotation).
-    yd = nv.dequant(q, s, g, rotate=True)
-    dq_ms = timed(lambda: nv.dequant(q, s, g, rotate=True, out=yd))
+    yd = nv.dequant(q, s, g, rotate=ROTATE)
+    dq_ms = timed(lambda: nv.dequant(q, s, g, rotate=ROTATE, out=yd))
     dq_bytes = n // 2 + n // 16 + 4 + 4 * n
     del y32, yd
 
     # parity spot check of the timed outputs against a second call (cheap)
-    q2, s2, g2, a2 = nv.rotquant(x, rotate=True)
+    q2, s2, g2, a2 = nv.rotquant(x, rotate=ROTATE)
     torch.cuda.synchronize()
     same = bool(torch.equal(q, q2) and torch.equal(s, s2) and torch.equal(g, g2))
 
-    traffic = load_traffic(n)
+    traffic = load_traffic(n) if WORKLOAD == DEFAULT_WORKLOAD else None
     out = {
-        "metric": "rotate+NVFP4-quantize GB/s and % of HBM peak, 16384x8192 bf16, 1 GPU",
+        "metric": f"rotate+NVFP4-quantize GB/s and % of HBM peak, {ROWS}x{COLS} {dname}, 1 GPU",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -315,9 +337,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "rows": ROWS, "cols": COLS, "input": "bf16",
-                   "rotate": True, "block": 16,
-                   "values": "student-t(3) x per-column lognormal(0,1) gain, seed 0",
+        "config": {"workload": WORKLOAD, "rows": ROWS, "cols": COLS, "input": dname,
+                   "rotate": ROTATE, "block": 16, "values": VALUES.get(WORKLOAD, WORKLOAD),
                    "cache": "warm" if args.no_flush else "cold (1 GiB read before each step)"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "elements_per_s": round(n / (ms * 1e-3), 1),
@@ -358,7 +379,7 @@ def main() -> int:
         "kernel_source_sha": kernel_source_sha(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w.x, True)
+        out["cpu_baseline"] = cpu_baseline(w.x, ROTATE, f"{ROWS}x{COLS} {dname}")
     print(json.dumps(out), flush=True)
     return 0
 

@@ -154,7 +154,7 @@ nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gsca
                            hipStream_t stream);
 
 /*
- * Measurement hook: nvfp4_rotquant (bf16), with every kernel it launches
+ * Measurement hook: nvfp4_rotquant (or _f32), with every kernel it launches
  * timed by HIP events that the runtime records at that kernel's own start and
  * end (hipExtLaunchKernel), so that a caller can time each pass of the fused
  * call in place, without the dispatch gap an event between launches adds.
@@ -166,13 +166,17 @@ nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gsca
  *             quantize pass) when q_out has room for pass 1's partial maxima,
  *             3 (zeroing, amax, quantize) for small tensors, 1 or 2 for
  *             empty ones.
- * Results are those of nvfp4_rotquant.  NVFP4_ERR_NULL when events or
- * nkernels is NULL or npairs < 1.
+ * Results are those of nvfp4_rotquant (nvfp4_rotquant_f32 for the _f32
+ * variant).  NVFP4_ERR_NULL when events or nkernels is NULL or npairs < 1.
  */
 nvfp4_status nvfp4_rotquant_timed(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,
                                   uint8_t *q_out, uint8_t *s_out, float *gscale_out,
                                   float *amax_out, hipStream_t stream, hipEvent_t *events,
                                   int npairs, int *nkernels);
+nvfp4_status nvfp4_rotquant_f32_timed(const float *x, int64_t rows, int64_t cols, int rotate,
+                                      uint8_t *q_out, uint8_t *s_out, float *gscale_out,
+                                      float *amax_out, hipStream_t stream, hipEvent_t *events,
+                                      int npairs, int *nkernels);
 
 /*
  * Block scales in the swizzled tiled layout (page "A Fused Hadamard + NVFP4

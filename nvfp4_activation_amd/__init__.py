@@ -48,6 +48,7 @@ _SIGS = {
     "nvfp4_rotate16": [_p, _i64, _i64, _p, _p],
     "nvfp4_rotquant_swizzled": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_rotquant_timed": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p, _p, _int, _p],
+    "nvfp4_rotquant_f32_timed": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p, _p, _int, _p],
     "nvfp4_rotquant_swizzled_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_dequant_swizzled": [_p, _p, _p, _i64, _i64, _int, _p, _p],
     "nvfp4_rotate16_f32": [_p, _i64, _i64, _p, _p],
@@ -159,13 +160,11 @@ def rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, str
 
 def rotquant_timed(x: torch.Tensor, events: list, rotate: bool = True, out: tuple | None = None,
                    stream=None):
-    """rotquant (bf16) with each launched kernel timed in place: events is a
-    list of torch.cuda.Event(enable_timing=True), each recorded once already;
-    kernel k records events[2k] and events[2k+1].  Returns (q, s, g, amax,
-    number of kernels launched)."""
+    """rotquant with each launched kernel timed in place: events is a list of
+    torch.cuda.Event(enable_timing=True), each recorded once already; kernel k
+    records events[2k] and events[2k+1].  Returns (q, s, g, amax, number of
+    kernels launched)."""
     rows, cols = _check_input(x)
-    if x.dtype != torch.bfloat16:
-        raise TypeError("rotquant_timed takes bfloat16 input")
     if out is None:
         q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
         s = torch.empty(rows, cols // 16, dtype=torch.uint8, device=x.device)
@@ -177,7 +176,8 @@ def rotquant_timed(x: torch.Tensor, events: list, rotate: bool = True, out: tupl
         raise ValueError("events must hold start/stop pairs")
     handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     nk = ctypes.c_int(0)
-    _check("nvfp4_rotquant_timed", lib.nvfp4_rotquant_timed(
+    fn = "nvfp4_rotquant_timed" if x.dtype == torch.bfloat16 else _variant(x, "nvfp4_rotquant") + "_timed"
+    _check(fn, getattr(lib, fn)(
         _ptr(x), rows, cols, int(bool(rotate)), _ptr(q), _ptr(s), _ptr(g), _ptr(a),
         _stream(x.device, stream), handles, len(events) // 2, ctypes.byref(nk)))
     return q, s, g, a, nk.value

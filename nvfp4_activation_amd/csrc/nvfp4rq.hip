@@ -378,6 +378,23 @@ nvfp4_status dequant(const uint8_t* q, const uint8_t* s, const float* gscale, in
   return NVFP4_OK;
 }
 
+// The fused call with the timing hook armed for this thread (see launch_impl).
+template <typename T>
+nvfp4_status timed(const T* x, int64_t rows, int64_t cols, int rotate, uint8_t* q, uint8_t* s,
+                   float* g, float* amax, hipStream_t st, hipEvent_t* events, int npairs,
+                   int* nkernels) {
+  if (!events || npairs < 1 || !nkernels) return NVFP4_ERR_NULL;
+  t_events = events;
+  t_pairs = npairs;
+  t_launched = 0;
+  const nvfp4_status r = rotquant(x, rows, cols, rotate, q, s, g, amax, st);
+  *nkernels = t_launched;
+  t_events = nullptr;
+  t_pairs = 0;
+  t_launched = 0;
+  return r;
+}
+
 }  // namespace
 }  // namespace nvfp4rq
 
@@ -397,17 +414,16 @@ nvfp4_status nvfp4_rotquant_timed(const uint16_t* x_bf16, int64_t rows, int64_t 
                                   uint8_t* q_out, uint8_t* s_out, float* gscale_out,
                                   float* amax_out, hipStream_t stream, hipEvent_t* events,
                                   int npairs, int* nkernels) {
-  if (!events || npairs < 1 || !nkernels) return NVFP4_ERR_NULL;
-  t_events = events;
-  t_pairs = npairs;
-  t_launched = 0;
-  const nvfp4_status r =
-      rotquant(x_bf16, rows, cols, rotate, q_out, s_out, gscale_out, amax_out, stream);
-  *nkernels = t_launched;
-  t_events = nullptr;
-  t_pairs = 0;
-  t_launched = 0;
-  return r;
+  return timed(x_bf16, rows, cols, rotate, q_out, s_out, gscale_out, amax_out, stream, events, npairs,
+               nkernels);
+}
+
+nvfp4_status nvfp4_rotquant_f32_timed(const float* x, int64_t rows, int64_t cols, int rotate,
+                                      uint8_t* q_out, uint8_t* s_out, float* gscale_out,
+                                      float* amax_out, hipStream_t stream, hipEvent_t* events,
+                                      int npairs, int* nkernels) {
+  return timed(x, rows, cols, rotate, q_out, s_out, gscale_out, amax_out, stream, events, npairs,
+               nkernels);
 }
 
 nvfp4_status nvfp4_rotquant_f32(const float* x, int64_t rows, int64_t cols, int rotate,

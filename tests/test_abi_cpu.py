@@ -41,7 +41,8 @@ def lib():
     for name in ("nvfp4_rotquant_swizzled", "nvfp4_rotquant_swizzled_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p]
     lib.nvfp4_dequant_swizzled.argtypes = [p, p, p, i64, i64, i, p, p]
-    lib.nvfp4_rotquant_timed.argtypes = [p, i64, i64, i, p, p, p, p, p, p, i, p]
+    for name in ("nvfp4_rotquant_timed", "nvfp4_rotquant_f32_timed"):
+        getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p, p, i, p]
     lib.nvfp4_swizzled_scale_bytes.argtypes = [i64, i64]
     lib.nvfp4_swizzled_scale_bytes.restype = i64
     lib.nvfp4_status_string.argtypes = [i]
@@ -56,7 +57,8 @@ def test_header_declares_the_boundary():
                  "mxfp4_rotquant", "mxfp4_rotquant_f32", "mxfp4_dequant",
                  "nvfp4_rotate16", "nvfp4_rotate16_f32", "nvfp4_rotquant_swizzled",
                  "nvfp4_rotquant_swizzled_f32", "nvfp4_dequant_swizzled",
-                 "nvfp4_swizzled_scale_bytes", "nvfp4_rotquant_timed"):
+                 "nvfp4_swizzled_scale_bytes", "nvfp4_rotquant_timed",
+                 "nvfp4_rotquant_f32_timed"):
         assert must in names
 
 
@@ -223,10 +225,11 @@ def test_swizzled_dequant_validation(lib):
     assert f(Q, S, G, 4, 64, 1, S - 64, None) == ERR_ARG
 
 
-def test_timed_validation(lib):
+@pytest.mark.parametrize("name", ["nvfp4_rotquant_timed", "nvfp4_rotquant_f32_timed"])
+def test_timed_validation(lib, name):
     """events and nkernels are host memory (an array of event handles and an
     int); validation runs before any event is touched."""
-    f = lib.nvfp4_rotquant_timed
+    f = getattr(lib, name)
     ev = (ctypes.c_void_p * 4)()
     nk = ctypes.c_int(-1)
     EV, NK = ctypes.addressof(ev), ctypes.addressof(nk)

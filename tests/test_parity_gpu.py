@@ -506,8 +506,9 @@ def test_head_wait_with_tiny_spin_limit(nv, monkeypatch):
 def test_timed_entry_point(nv):
     """The measurement hook gives the fused call's bytes, reports the kernels
     it launched and leaves each kernel's duration in its event pair."""
-    for rows, cols, want in ((2048, 4096, 2), (4, 64, 3)):
-        x = mixed_input(rows, cols, "bf16", seed=rows)
+    for rows, cols, want, dtype in ((2048, 4096, 2, "bf16"), (4, 64, 3, "bf16"),
+                                    (2048, 4096, 2, "f32")):
+        x = mixed_input(rows, cols, dtype, seed=rows)
         xd = to_dev(x)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         for e in ev:
@@ -516,7 +517,7 @@ def test_timed_entry_point(nv):
         q, s, g, a, nk = nv.rotquant_timed(xd, ev)
         torch.cuda.synchronize()
         assert nk == want
-        compare(f"timed {rows}x{cols}", x, True, (q, s, g, a))
+        compare(f"timed {rows}x{cols} {dtype}", x, True, (q, s, g, a))
         for k in range(nk):
             ms = ev[2 * k].elapsed_time(ev[2 * k + 1])
             assert 0.0 < ms < 100.0, (k, ms)

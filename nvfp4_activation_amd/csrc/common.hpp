@@ -25,7 +25,7 @@ constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
 // (possible only when the global scale comes from another tensor's amax) take
 // true divisions.
 constexpr float kQuotientLimit = 0x1p100f;
-constexpr int64_t kLastLevelKeep = 176LL << 20;  // bytes of input pass 1 leaves cached
+constexpr int64_t kLastLevelKeep = 144LL << 20;  // bytes of input pass 1 leaves cached
 // Arrival counters of the quantize pass when pass 1 leaves its partial maxima
 // in q_out: spread over kCounters words on separate 128-byte lines, since
 // thousands of increments of one word serialize (and a workgroup's loads

@@ -190,9 +190,10 @@ hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* b
   // The quantize pass walks the tensor last-first and finds the part pass 1
   // read last in the 256 MB last-level cache; the part before the last
   // kLastLevelKeep bytes would be evicted before the quantize pass got to it,
-  // so pass 1 streams it with non-temporal loads (measured at 16384 x 8192:
-  // 1 us off pass 1, nothing lost in pass 2; streaming more costs pass 2 its
-  // cache hits).
+  // so pass 1 streams it with non-temporal loads.  Measured at 16384 x 8192
+  // (step, keeping 96 / 128 / 144 / 176 / 240 MB): 103.5 / 101.0 / 100.9 /
+  // 101.0 / 102.5 us; streaming less leaves pass 1 slower, streaming more
+  // costs pass 2 its cache hits.  At 32768 x 14336 the rule takes 12 us off.
   const int64_t keep_mb = env_int("NVFP4RQ_LLC_KEEP_MB");
   const int64_t keep_pieces = (keep_mb ? keep_mb << 20 : kLastLevelKeep) / 16;
   const int64_t nt_end = 2 * nb > keep_pieces ? 2 * nb - keep_pieces : 0;

@@ -199,7 +199,7 @@ def main() -> int:
     gbs = nbytes["step"] / (ms * 1e-3) / 1e9
 
     # Context: the same step replayed as a captured HIP graph (launch path of
-    # serving loops); the captured work is the identical three kernels.
+    # serving loops); the captured work is the identical two kernels.
     graph_ms = None
     if args.graph:
         side = torch.cuda.Stream()

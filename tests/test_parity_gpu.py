@@ -621,3 +621,23 @@ def test_given_scale_and_decode_at_bench_size(nv):
     yd = oracle.dequant_f64(qn, sn, gn, True)
     err = np.abs(y.cpu().numpy().astype(np.float64) - yd).reshape(-1, 16)
     assert np.all(err <= 1e-6 * np.abs(yd).reshape(-1, 16).max(1, keepdims=True))
+
+
+@pytest.mark.parametrize("nb", [1039, 1040, 1041, 2047, 2048, 2049, 4101])
+def test_partials_path_threshold(nv, monkeypatch, nb):
+    """Around the size from which pass 1's maxima and counters fit at the head
+    of q_out (about 1040 blocks), in one row and in one column of blocks, with
+    the default grid and with pass-2 grids of 1 and 7 workgroups (one
+    workgroup then owns every chunk that overlaps the head)."""
+    for rows, cols in ((1, 16 * nb), (nb, 16)):
+        x = mixed_input(rows, cols, "bf16", seed=nb + rows)
+        xd = to_dev(x)
+        ref = oracle.quantize(x, True)
+        for q_wgs in (None, 1, 7):
+            if q_wgs is None:
+                monkeypatch.delenv("NVFP4RQ_QUANT_WGS", raising=False)
+            else:
+                monkeypatch.setenv("NVFP4RQ_QUANT_WGS", str(q_wgs))
+            got = nv.rotquant(xd)
+            torch.cuda.synchronize()
+            compare(f"nb={nb} {rows}x{cols} quant_wgs={q_wgs}", x, True, got, ref)

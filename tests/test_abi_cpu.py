@@ -239,3 +239,24 @@ def test_timed_validation(lib, name):
     assert f(X, 4, 40, 1, Q, S, G, A, None, EV, 2, NK) == ERR_SHAPE
     assert nk.value == 0                     # nothing launched
     assert f(X, 4, 64, 1, X, S, G, A, None, EV, 2, NK) == ERR_ARG
+
+
+def test_header_is_a_c_interface(tmp_path):
+    """A C11 program (gcc, no C++) includes the header, links the library and
+    calls the one entry point that needs no device: the header is a C
+    interface usable without PyTorch or a C++ compiler."""
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include <stdio.h>\n#include "nvfp4rq.h"\n'
+                   'int main(void) {\n'
+                   '  printf("%s|%s\\n", nvfp4_status_string(NVFP4_OK),\n'
+                   '         nvfp4_status_string(NVFP4_ERR_SHAPE));\n'
+                   '  return 0;\n}\n')
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(LIB)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    f"-L{libdir}", "-lnvfp4rq", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.strip()
+    ok, shape = out.split("|")
+    assert ok and shape and ok != shape

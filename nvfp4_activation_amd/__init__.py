@@ -111,12 +111,45 @@ def _check_input(x: torch.Tensor) -> tuple[int, int]:
     return x.shape[0], x.shape[1]
 
 
+def _buf(t, numel: int, dtype: torch.dtype, device: torch.device, name: str) -> torch.Tensor:
+    """A caller-supplied buffer: the library receives only its address, so the
+    dtype, device, layout and size are checked here, before any launch."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the input on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    return t
+
+
+def _check_out4(x, rows, cols, q, s, g, a, s_numel):
+    _buf(q, rows * cols // 2, torch.uint8, x.device, "q")
+    _buf(s, s_numel, torch.uint8, x.device, "s")
+    _buf(g, 1, torch.float32, x.device, "g")
+    _buf(a, 1, torch.float32, x.device, "amax")
+
+
+def _decode_inputs(q, s, g, s_numel):
+    if not q.is_cuda:
+        raise ValueError("q must be a device tensor")
+    _buf(q, q.numel(), torch.uint8, q.device, "q")
+    _buf(s, s_numel, torch.uint8, q.device, "s")
+    if g is not None:
+        _buf(g, 1, torch.float32, q.device, "g")
+
+
 def rotamax(x: torch.Tensor, rotate: bool = True, amax: torch.Tensor | None = None,
             stream=None) -> torch.Tensor:
     """Pass 1: the rotated global amax, as a float32 device tensor [1]."""
     rows, cols = _check_input(x)
     if amax is None:
         amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    _buf(amax, 1, torch.float32, x.device, "amax")
     fn = _variant(x, "nvfp4_rotamax")
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(amax),
                                 _stream(x.device, stream)))
@@ -134,6 +167,10 @@ def quant_from_amax(x: torch.Tensor, amax: torch.Tensor, rotate: bool = True,
         g = torch.empty(1, dtype=torch.float32, device=x.device)
     else:
         q, s, g = out
+    _buf(amax, 1, torch.float32, x.device, "amax")
+    _buf(q, rows * cols // 2, torch.uint8, x.device, "q")
+    _buf(s, rows * cols // 16, torch.uint8, x.device, "s")
+    _buf(g, 1, torch.float32, x.device, "g")
     fn = _variant(x, "nvfp4_quant_from_amax")
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(amax), _ptr(q),
                                 _ptr(s), _ptr(g), _stream(x.device, stream)))
@@ -152,6 +189,7 @@ def rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, str
         a = torch.empty(1, dtype=torch.float32, device=x.device)
     else:
         q, s, g, a = out
+    _check_out4(x, rows, cols, q, s, g, a, rows * cols // 16)
     fn = _variant(x, "nvfp4_rotquant")
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(q), _ptr(s),
                                 _ptr(g), _ptr(a), _stream(x.device, stream)))
@@ -172,6 +210,7 @@ def rotquant_timed(x: torch.Tensor, events: list, rotate: bool = True, out: tupl
         a = torch.empty(1, dtype=torch.float32, device=x.device)
     else:
         q, s, g, a = out
+    _check_out4(x, rows, cols, q, s, g, a, rows * cols // 16)
     if len(events) < 2 or len(events) % 2:
         raise ValueError("events must hold start/stop pairs")
     handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
@@ -192,8 +231,10 @@ def dequant(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = Tr
     rows, cols = s.shape[0], s.shape[1] * 16
     if q.shape != (rows, cols // 2):
         raise ValueError("q and s shapes disagree")
+    _decode_inputs(q, s, g, s.numel())
     if out is None:
         out = torch.empty(rows, cols, dtype=torch.float32, device=q.device)
+    _buf(out, rows * cols, torch.float32, q.device, "out")
     _check("nvfp4_dequant", lib.nvfp4_dequant(_ptr(q), _ptr(s), _ptr(g), rows, cols,
                                               int(bool(rotate)), _ptr(out),
                                               _stream(q.device, stream)))
@@ -218,6 +259,7 @@ def rotquant_swizzled(x: torch.Tensor, rotate: bool = True, out: tuple | None = 
         a = torch.empty(1, dtype=torch.float32, device=x.device)
     else:
         q, s, g, a = out
+    _check_out4(x, rows, cols, q, s, g, a, swizzled_scale_bytes(rows, cols))
     fn = _variant(x, "nvfp4_rotquant_swizzled")
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(q), _ptr(s),
                                 _ptr(g), _ptr(a), _stream(x.device, stream)))
@@ -226,9 +268,13 @@ def rotquant_swizzled(x: torch.Tensor, rotate: bool = True, out: tuple | None = 
 
 def dequant_swizzled(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = True,
                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if q.dim() != 2:
+        raise ValueError("q must be 2-D [rows, cols/2]")
     rows, cols = q.shape[0], q.shape[1] * 2
+    _decode_inputs(q, s, g, swizzled_scale_bytes(rows, cols))
     if out is None:
         out = torch.empty(rows, cols, dtype=torch.float32, device=q.device)
+    _buf(out, rows * cols, torch.float32, q.device, "out")
     _check("nvfp4_dequant_swizzled", lib.nvfp4_dequant_swizzled(
         _ptr(q), _ptr(s), _ptr(g), rows, cols, int(bool(rotate)), _ptr(out),
         _stream(q.device, stream)))
@@ -240,6 +286,7 @@ def rotate16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> t
     rows, cols = _check_input(x)
     if out is None:
         out = torch.empty(rows, cols, dtype=torch.float32, device=x.device)
+    _buf(out, rows * cols, torch.float32, x.device, "out")
     fn = _variant(x, "nvfp4_rotate16")
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, _ptr(out), _stream(x.device, stream)))
     return out
@@ -254,6 +301,8 @@ def mx_rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, 
         s = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)
     else:
         q, s = out
+    _buf(q, rows * cols // 2, torch.uint8, x.device, "q")
+    _buf(s, rows * cols // 32, torch.uint8, x.device, "s")
     fn = _variant(x, "mxfp4_rotquant")
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, int(bool(rotate)), _ptr(q), _ptr(s),
                                 _stream(x.device, stream)))
@@ -262,11 +311,15 @@ def mx_rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, 
 
 def mx_dequant(q: torch.Tensor, s: torch.Tensor, rotate: bool = True,
                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if s.dim() != 2 or q.dim() != 2:
+        raise ValueError("q and s must be 2-D")
     rows, cols = s.shape[0], s.shape[1] * 32
     if q.shape != (rows, cols // 2):
         raise ValueError("q and s shapes disagree")
+    _decode_inputs(q, s, None, s.numel())
     if out is None:
         out = torch.empty(rows, cols, dtype=torch.float32, device=q.device)
+    _buf(out, rows * cols, torch.float32, q.device, "out")
     _check("mxfp4_dequant", lib.mxfp4_dequant(_ptr(q), _ptr(s), rows, cols, int(bool(rotate)),
                                               _ptr(out), _stream(q.device, stream)))
     return out

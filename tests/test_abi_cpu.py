@@ -260,3 +260,23 @@ def test_header_is_a_c_interface(tmp_path):
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.strip()
     ok, shape = out.split("|")
     assert ok and shape and ok != shape
+
+
+def test_binding_buffer_checks_on_host():
+    """The binding's buffer check is host logic: exercise it with host tensors."""
+    import torch
+    import nvfp4_activation_amd as nv
+    cpu = torch.device("cpu")
+    ok = torch.empty(8, dtype=torch.uint8)
+    assert nv._buf(ok, 8, torch.uint8, cpu, "q") is ok
+    assert nv._buf(torch.empty(9, dtype=torch.uint8), 8, torch.uint8, cpu, "q") is not None
+    with pytest.raises(ValueError, match="7 elements, 8 needed"):
+        nv._buf(torch.empty(7, dtype=torch.uint8), 8, torch.uint8, cpu, "q")
+    with pytest.raises(TypeError, match="uint8"):
+        nv._buf(torch.empty(8, dtype=torch.int8), 8, torch.uint8, cpu, "q")
+    with pytest.raises(ValueError, match="contiguous"):
+        nv._buf(torch.empty(16, dtype=torch.uint8)[::2], 8, torch.uint8, cpu, "q")
+    with pytest.raises(ValueError, match="is on"):
+        nv._buf(ok, 8, torch.uint8, torch.device("cuda", 0), "q")
+    with pytest.raises(TypeError, match="tensor"):
+        nv._buf(None, 8, torch.uint8, cpu, "q")

@@ -5,9 +5,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "nvfp4rq_device.hpp"
 #include "common.hpp"
+#include "pass2.hpp"
 
 namespace nvfp4rq {
 namespace {  // one translation unit (nvfp4rq.hip): internal linkage
@@ -33,46 +35,118 @@ __device__ __forceinline__ void load_quarter(const uint16_t* __restrict__ x, int
   z[0] = bf16_lo(v.x); z[1] = bf16_hi(v.x); z[2] = bf16_lo(v.y); z[3] = bf16_hi(v.y);
 }
 
-// Dequantize (section 2, dequantize): +-GRID[c & 7] * RN(float(s) * g), then
-// the same butterfly and * 0.25 when rotated (H16 is symmetric, so H16^T is
-// the forward transform).  nq = number of quarters = rows * cols / 4.
+// ---------------------------------------------------------------- decode
+
+// The decode kernels give each wave one slice of kSliceQuarters consecutive
+// quarters (2048 outputs) and launch one wave per slice.  A wave stages its
+// slice's codes (1 KiB: two 8-byte loads per lane) and, for row-major scales,
+// its scale bytes (one or two byte loads per lane) in its own part of LDS, and
+// reads them back in the quarter layout.  At 16384 x 8192 this runs the
+// rotated decode in 90 us where per-quarter code and scale loads in a grid of
+// 8 persistent workgroups per CU took 123 us: the 512 MiB of fp32 stores run
+// at the chip's write rate only when the few reads between them are issued
+// early, as few wide loads, by waves that do not come back for more.
+constexpr int64_t kSliceQuarters = 64 * kQuarters;
+
+// Where a decode kernel finds the scale of a quarter and what a scale byte
+// stands for.
 template <typename SMAP>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ q,
-                                                           const uint8_t* __restrict__ s,
-                                                           const float* __restrict__ gscale,
-                                                           int64_t nq, int rotate,
-                                                           float* __restrict__ y, SMAP smap) {
-  const uint32_t lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  constexpr int64_t kPerWave = 64 * kQuarters;
-  const uint16_t* __restrict__ q2 = reinterpret_cast<const uint16_t*>(q);  // 4 codes
+struct Nvfp4Scales {  // one E4M3 byte per 16-element block: RN(float(s) * g)
+  static constexpr int kQuartersPerScale = 4;
+  // row-major: a slice's scale bytes are consecutive and are staged with its
+  // codes; swizzled: each quarter reads its byte where the layout puts it
+  static constexpr bool kStaged = std::is_same<SMAP, RowMajorScales>::value;
+  SMAP smap;
+  __device__ __forceinline__ int64_t index(int64_t block) const { return smap(block); }
+  __device__ __forceinline__ float factor(uint32_t b, float g) const { return e4m3_value(b) * g; }
+};
+struct Mxfp4Scales {  // one E8M0 byte per 32-element block: 2^(byte - 127), exact
+  static constexpr int kQuartersPerScale = 8;
+  static constexpr bool kStaged = true;
+  __device__ __forceinline__ int64_t index(int64_t block) const { return block; }
+  __device__ __forceinline__ float factor(uint32_t b, float) const {
+    return ldexpf(1.0f, static_cast<int>(b) - 127);
+  }
+};
+
+// Hand-over through LDS inside one wave: the wave's stores are complete and
+// visible to its own later loads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Decode (section 2, dequantize): +-GRID[c & 7] * scale factor, each product a
+// binary32 multiply, then the same butterfly and * 0.25 when rotated (H16 is
+// symmetric, so H16^T is the forward transform).  nq = number of quarters;
+// gscale may be null for scales that need no global factor (MXFP4).
+// TAIL = false: the waves take the nq / kSliceQuarters whole slices, with no
+// bounds checks (a store burst broken up by per-lane guards costs 10% here);
+// TAIL = true: one wave takes the partial slice at the end, if there is one.
+template <typename SRC, bool ROTATE, bool TAIL>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restrict__ q,
+                                                          const uint8_t* __restrict__ s,
+                                                          const float* __restrict__ gscale,
+                                                          int64_t nq, float* __restrict__ y, SRC src) {
+  constexpr int kScaleBytes = static_cast<int>(kSliceQuarters) / SRC::kQuartersPerScale;
+  __shared__ uint2 codes[kThreads / 64][kSliceQuarters / 4];
+  __shared__ uint8_t scales[kThreads / 64][SRC::kStaged ? kScaleBytes : 1];
+  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nslices = TAIL ? (nq % kSliceQuarters != 0) : nq / kSliceQuarters;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x / 64);
+  uint16_t* c16 = reinterpret_cast<uint16_t*>(&codes[wv][0]);
   float4* __restrict__ o = reinterpret_cast<float4*>(y);
-  const float g = *gscale;
-  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
-    uint32_t c[kQuarters], sb[kQuarters];
+  const float g = gscale ? *gscale : 1.0f;
+  for (int64_t w = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x * (blockDim.x / 64) + wv));
+       w < nslices; w += nwaves) {
+    const int64_t base = (TAIL ? nq / kSliceQuarters : w) * kSliceQuarters;
+    const int64_t first = base / SRC::kQuartersPerScale;
+    if (!TAIL) {
+      const uint2* __restrict__ q8 = reinterpret_cast<const uint2*>(q);
+      codes[wv][lane] = q8[(base >> 2) + lane];
+      codes[wv][lane + 64] = q8[(base >> 2) + 64 + lane];
+      if constexpr (SRC::kStaged) {
 #pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      const int64_t pc = base + j * 64 + lane;
-      const bool in = pc < nq;
-      c[j] = in ? q2[pc] : 0u;
-      sb[j] = in ? s[smap(pc >> 2)] : 0u;
+        for (int i = 0; i < kScaleBytes; i += 64) scales[wv][i + lane] = s[first + i + lane];
+      }
+    } else {
+      const uint16_t* __restrict__ q2 = reinterpret_cast<const uint16_t*>(q);
+      const int64_t nscales = nq / SRC::kQuartersPerScale;
+#pragma unroll
+      for (int j = 0; j < kQuarters; ++j) {
+        const int64_t pc = base + j * 64 + lane;
+        c16[j * 64 + lane] = pc < nq ? q2[pc] : uint16_t{0};
+      }
+      if constexpr (SRC::kStaged) {
+#pragma unroll
+        for (int i = 0; i < kScaleBytes; i += 64)
+          scales[wv][i + lane] = first + i + lane < nscales ? s[first + i + lane] : uint8_t{0};
+      }
     }
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < kQuarters; ++j) {
-      const float sf = e4m3_value(sb[j]) * g;
-      float z[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = e2m1_value((c[j] >> (4 * i)) & 15u) * sf;
-      if (rotate) {
+      const uint32_t qi = j * 64 + lane;
+      const int64_t pc = base + qi;
+      const uint32_t c = c16[qi];
+      uint32_t sb;
+      if constexpr (SRC::kStaged)
+        sb = scales[wv][qi / SRC::kQuartersPerScale];
+      else
+        sb = (!TAIL || pc < nq) ? s[src.index(pc / SRC::kQuartersPerScale)] : 0u;
+      const float f = src.factor(sb, g);
+      const float2 v01 = e2m1_pair<0>(c), v23 = e2m1_pair<1>(c);
+      float z[4] = {v01.x * f, v01.y * f, v23.x * f, v23.y * f};
+      if (ROTATE) {
         stages_1_2(z);
         quad_stages_4_8(z, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = 0.25f * z[i];
       }
-      const int64_t pc = base + j * 64 + lane;
-      if (pc < nq) o[pc] = make_float4(z[0], z[1], z[2], z[3]);
+      if (!TAIL || pc < nq) o[pc] = make_float4(z[0], z[1], z[2], z[3]);
     }
+    wave_lds_sync();  // the slice's LDS is rewritten by the next iteration
   }
 }
 
@@ -115,47 +189,6 @@ __global__ __launch_bounds__(kThreads) void rotate_kernel(const T* __restrict__ 
       const int64_t pc = base + j * 64 + lane;
       if (pc < nq)
         o[pc] = make_float4(0.25f * z[j][0], 0.25f * z[j][1], 0.25f * z[j][2], 0.25f * z[j][3]);
-    }
-  }
-}
-
-// MXFP4 dequantize: +-GRID[c & 7] * 2^(byte - 127), rounded to binary32, then
-// the inverse rotation of each 16-element half (the same butterfly and
-// * 0.25).  Quarter-block layout as for the NVFP4 decode; a 32-element block
-// is two quads.
-__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ q,
-                                                              const uint8_t* __restrict__ s,
-                                                              int64_t nq, int rotate,
-                                                              float* __restrict__ y) {
-  const uint32_t lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  constexpr int64_t kPerWave = 64 * kQuarters;
-  const uint16_t* __restrict__ q2 = reinterpret_cast<const uint16_t*>(q);
-  float4* __restrict__ o = reinterpret_cast<float4*>(y);
-  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
-    uint32_t c[kQuarters], sb[kQuarters];
-#pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      const int64_t pc = base + j * 64 + lane;
-      const bool in = pc < nq;
-      c[j] = in ? q2[pc] : 0u;
-      sb[j] = in ? s[pc >> 3] : 127u;
-    }
-#pragma unroll
-    for (int j = 0; j < kQuarters; ++j) {
-      const float sc = ldexpf(1.0f, static_cast<int>(sb[j]) - 127);
-      float z[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = e2m1_value((c[j] >> (4 * i)) & 15u) * sc;
-      if (rotate) {
-        stages_1_2(z);
-        quad_stages_4_8(z, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = 0.25f * z[i];
-      }
-      const int64_t pc = base + j * 64 + lane;
-      if (pc < nq) o[pc] = make_float4(z[0], z[1], z[2], z[3]);
     }
   }
 }

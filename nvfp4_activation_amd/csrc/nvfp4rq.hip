@@ -135,6 +135,24 @@ int quarter_grid(int64_t nq) {
   return clamp_grid(8LL * device_cus(), (nq + per_wg - 1) / per_wg);
 }
 
+// Decode: one wave per whole slice of kSliceQuarters quarters, then one wave
+// for a partial slice at the end.
+template <bool ROTATE, typename SRC>
+nvfp4_status launch_decode(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t nq,
+                           float* y, SRC src, hipStream_t st) {
+  const int64_t per_wg = (kThreads / 64) * kSliceQuarters;
+  const int64_t whole = nq / kSliceQuarters;
+  if (whole > 0 && launch(decode_kernel<SRC, ROTATE, false>,
+                          dim3(clamp_grid((nq + per_wg - 1) / per_wg, (nq + per_wg - 1) / per_wg)),
+                          dim3(kThreads), st, q, s, gscale, nq, y, src) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  if (nq % kSliceQuarters != 0 &&
+      launch(decode_kernel<SRC, ROTATE, true>, dim3(1), dim3(64), st, q, s, gscale, nq, y, src) !=
+          hipSuccess)
+    return NVFP4_ERR_HIP;
+  return NVFP4_OK;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 struct Range {
@@ -225,13 +243,24 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const uint32_t* a
                            int npartials, float* amax_out, uint8_t* q, uint8_t* s, float* g,
                            hipStream_t st, SMAP smap = SMAP{}) {
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
-  // bf16: visit chunks on the XCD whose L2 pass 1 left them in (see
-  // RowMajorScales::order); fp32's pass 1 already reads chunk c on XCD c % 8.
-  if constexpr (std::is_same_v<SMAP, RowMajorScales> && sizeof(T) == 2)
-    smap.xcd_order = smap.chunks(nb) % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
+  const int64_t nchunks = smap.chunks(nb);
+  dim3 grid(quant_grid(nchunks * kThreads));
+  if constexpr (std::is_same_v<SMAP, RowMajorScales>) {
+    if (npartials == 0) {
+      // Amax given as a word: the workgroup prologue is a single load, and a
+      // workgroup per chunk beats 8 persistent ones per CU (16384 x 8192 bf16,
+      // cold: 62 against 68 us); with per-workgroup maxima to reduce first,
+      // the persistent grid stays ahead.
+      grid = dim3(clamp_grid(nchunks, nchunks));
+      smap.mirror = 1;
+    } else if constexpr (sizeof(T) == 2) {
+      // bf16: visit chunks on the XCD whose L2 pass 1 left them in (see
+      // RowMajorScales::order); fp32's pass 1 already reads chunk c on XCD c % 8.
+      smap.xcd_order = nchunks % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
+    }
+  }
   const int64_t spin_env = env_int("NVFP4RQ_SPIN_LIMIT");
   const uint32_t spin_limit = spin_env > 0 ? static_cast<uint32_t>(spin_env) : (1u << 26);
-  const dim3 grid(quant_grid(smap.chunks(nb) * kThreads));
   const hipError_t e =
       rotate ? launch(rotquant_kernel<T, true, SMAP>, grid, dim3(kThreads), st, x, nb, amax_src,
                       npartials, amax_out, spin_limit, allow_fast, q, s, g, smap)
@@ -332,7 +361,9 @@ nvfp4_status mx_rotquant(const T* x, int64_t rows, int64_t cols, int rotate, uin
   if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return NVFP4_ERR_ARG;
   const int64_t nb32 = n / 32;
   if (nb32 == 0) return NVFP4_OK;
-  const dim3 grid(quant_grid(nb32));
+  // a workgroup per 256 blocks (16384 x 8192 bf16, cold: 58 us against 62
+  // with 8 persistent workgroups per CU)
+  const dim3 grid(clamp_grid((nb32 + kThreads - 1) / kThreads, (nb32 + kThreads - 1) / kThreads));
   const hipError_t e = rotate ? launch(mx_quant_kernel<T, true>, grid, dim3(kThreads), st, x, nb32, q, s)
                               : launch(mx_quant_kernel<T, false>, grid, dim3(kThreads), st, x, nb32, q, s);
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
@@ -373,10 +404,8 @@ nvfp4_status dequant(const uint8_t* q, const uint8_t* s, const float* gscale, in
     return NVFP4_ERR_ARG;
   if (nb == 0) return NVFP4_OK;
   const int64_t nq = 4 * nb;
-  if (launch(dequant_kernel<SMAP>, dim3(quarter_grid(nq)), dim3(kThreads), stream, q, s, gscale, nq,
-             rotate, y_out, smap) != hipSuccess)
-    return NVFP4_ERR_HIP;
-  return NVFP4_OK;
+  return rotate ? launch_decode<true>(q, s, gscale, nq, y_out, Nvfp4Scales<SMAP>{smap}, stream)
+                : launch_decode<false>(q, s, gscale, nq, y_out, Nvfp4Scales<SMAP>{smap}, stream);
 }
 
 // The fused call with the timing hook armed for this thread (see launch_impl).
@@ -519,10 +548,9 @@ nvfp4_status mxfp4_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int
   const int64_t nb32 = n / 32;
   if (nb32 == 0) return NVFP4_OK;
   const int64_t nq = 8 * nb32;
-  if (launch(mx_dequant_kernel, dim3(quarter_grid(nq)), dim3(kThreads), stream, q, s, nq, rotate,
-             y_out) != hipSuccess)
-    return NVFP4_ERR_HIP;
-  return NVFP4_OK;
+  const float* no_gscale = nullptr;
+  return rotate ? launch_decode<true>(q, s, no_gscale, nq, y_out, Mxfp4Scales{}, stream)
+                : launch_decode<false>(q, s, no_gscale, nq, y_out, Mxfp4Scales{}, stream);
 }
 
 const char* nvfp4_status_string(nvfp4_status status) {

@@ -162,13 +162,19 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float q[8]) {
   return w;
 }
 
-// Signed grid value of an E2M1 code: +-{0, .5, 1, 1.5, 2, 3, 4, 6}[c & 7]
-// (section 1 table; section 2, dequantize's GRID).
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const float mag = m < 4u ? 0.5f * static_cast<float>(m)
-                           : static_cast<float>(2u << ((m - 4u) >> 1)) * ((m & 1u) ? 1.5f : 1.0f);
-  return (c & 8u) ? -mag : mag;
+// Signed grid values of the two E2M1 codes in byte BYTE of w, element 2k in
+// the low nibble (section 1 table; section 2, dequantize's GRID):
+// +-{0, .5, 1, 1.5, 2, 3, 4, 6}[c & 7], code 8 giving -0.0 like the page's
+// sign flip of a zero magnitude.  The gfx950 conversion
+// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 returns both values exactly; a
+// check of all 256 bytes at each of the four byte positions matches the table
+// bit for bit (tests/test_instructions_gpu.py).  Only the exponent of the
+// scale operand enters the instruction, so the block scale is applied by an
+// ordinary binary32 multiply afterwards.
+template <int BYTE>
+__device__ __forceinline__ float2 e2m1_pair(uint32_t w) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BYTE);
+  return make_float2(v[0], v[1]);
 }
 
 // ---------------------------------------------------------------- scales

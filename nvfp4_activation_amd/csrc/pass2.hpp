@@ -30,6 +30,7 @@ struct RowMajorScales {
   static constexpr int kSub = 1;
   static constexpr bool kStaged = false;
   int xcd_order;  // visit chunks on the XCD that read them in pass 1
+  int mirror;     // a workgroup per chunk, workgroup i taking chunk nchunks - 1 - i
   __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
   __host__ __device__ int64_t chunks(int64_t nb) const { return (nb + kThreads - 1) / kThreads; }
   // Workgroups go round-robin to the 8 XCDs, each with its own L2, and the L2
@@ -40,7 +41,11 @@ struct RowMajorScales {
   // its own XCD.  At 16384 x 8192 this takes 5 us off the pass on a box whose
   // last-level cache gave it nothing.  Set only when the chunk count is a
   // multiple of 32, so the order is a permutation of the chunks.
-  __device__ __forceinline__ int64_t order(int64_t i, int64_t) const {
+  // With a workgroup per chunk the dispatcher starts workgroups in index
+  // order, so mirror keeps the last chunks (the likeliest to be still cached
+  // after an amax pass) first.
+  __device__ __forceinline__ int64_t order(int64_t i, int64_t nchunks) const {
+    if (mirror) return nchunks - 1 - i;
     return xcd_order ? (i & ~int64_t{31}) | ((i & 7) << 2) | ((i >> 3) & 3) : i;
   }
   __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const { return chunk * kThreads * 8; }

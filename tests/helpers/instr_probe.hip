@@ -33,11 +33,24 @@ __global__ void pack_kernel(const float* __restrict__ v, uint32_t* __restrict__ 
   out[1] = e2m1_pack8(b);
 }
 
-// all 256 E4M3 byte values -> float (e4m3_value) and all 16 codes -> e2m1_value
+// all 256 E4M3 byte values -> float (e4m3_value); every byte at each of the
+// four positions of a word -> its two E2M1 values (e2m1_pair), the other
+// bytes holding junk: e2m1[2 (256 pos + byte) + k]
 __global__ void values_kernel(float* __restrict__ e4m3, float* __restrict__ e2m1) {
   const uint32_t i = threadIdx.x;
   e4m3[i] = e4m3_value(i);
-  if (i < 16) e2m1[i] = e2m1_value(i);
+  const uint32_t junk = 0xA5C3963Cu;
+#pragma unroll
+  for (int pos = 0; pos < 4; ++pos) {
+    const uint32_t w = (junk & ~(0xFFu << (8 * pos))) | (i << (8 * pos));
+    float2 v;
+    if (pos == 0) v = e2m1_pair<0>(w);
+    else if (pos == 1) v = e2m1_pair<1>(w);
+    else if (pos == 2) v = e2m1_pair<2>(w);
+    else v = e2m1_pair<3>(w);
+    e2m1[2 * (256 * pos + i)] = v.x;
+    e2m1[2 * (256 * pos + i) + 1] = v.y;
+  }
 }
 
 extern "C" {
@@ -53,6 +66,7 @@ int probe_pack(const float* v, uint32_t* out, hipStream_t st) {
   pack_kernel<<<1, 1, 0, st>>>(v, out);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
+// e4m3: 256 floats; e2m1: 2048 floats
 int probe_values(float* e4m3, float* e2m1, hipStream_t st) {
   values_kernel<<<1, 256, 0, st>>>(e4m3, e2m1);
   return hipGetLastError() == hipSuccess ? 0 : 1;

@@ -10,6 +10,8 @@ through the library's own device helpers, against the CPU oracle.
 - E4M3: min(v, 448) then v_cvt_pk_fp8_f32 behind e4m3_byte, every binary32
   in [0, +inf], against the oracle's round-to-nearest-even with the 448 clamp
   (section 2, _round_e4m3; section 3).
+- Decode: v_cvt_scalef32_pk_f32_fp4 (scale 1.0) behind e2m1_pair, every byte
+  at every byte position, against the grid table of section 1, bit for bit.
 """
 from __future__ import annotations
 
@@ -92,11 +94,19 @@ def test_nibble_order_and_value_tables(probe):
     codes = [(int(w[i // 8]) >> (4 * (i % 8))) & 15 for i in range(16)]
     assert codes == [oracle.e2m1_code(float(t)) for t in v.cpu().numpy()]
     e4 = torch.zeros(256, dtype=torch.float32, device="cuda:0")
-    e2 = torch.zeros(16, dtype=torch.float32, device="cuda:0")
+    e2 = torch.zeros(2048, dtype=torch.float32, device="cuda:0")
     probe.probe_values(e4.data_ptr(), e2.data_ptr(), _stream())
     torch.cuda.synchronize()
     e4 = e4.cpu().numpy()
     for b in range(127):
         assert e4[b] == oracle.e4m3_value(b), b
-    grid = [0, .5, 1, 1.5, 2, 3, 4, 6]
-    assert list(e2.cpu().numpy()) == grid + [-g for g in grid]
+    # E2M1 decode (v_cvt_scalef32_pk_f32_fp4, scale 1.0): every byte at every
+    # byte position, low nibble first, compared as bits so that code 8 must
+    # give -0.0 (the page's dequantize flips the sign of a zero magnitude)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    table = np.concatenate([grid, -grid]).astype(np.float32)
+    byte = np.arange(256)
+    want = np.stack([table[byte & 15], table[byte >> 4]], axis=1).reshape(-1)
+    got = e2.cpu().numpy().reshape(4, 512)
+    for pos in range(4):
+        assert np.array_equal(got[pos].view(np.uint32), want.view(np.uint32)), pos

@@ -128,11 +128,11 @@ int quant_grid(int64_t nb) {
 
 int generic_grid(int64_t nb) { return clamp_grid(8LL * device_cus(), (nb + kThreads - 1) / kThreads); }
 
-// Quarter-block kernels: 8 workgroups per compute unit, kThreads * kQuarters
-// quarters per workgroup iteration.
+// Rotation alone: one workgroup per kThreads * kQuarters quarters (16384 x
+// 8192 bf16: 123 us against 128 with 8 persistent workgroups per CU).
 int quarter_grid(int64_t nq) {
   const int64_t per_wg = static_cast<int64_t>(kThreads) * kQuarters;
-  return clamp_grid(8LL * device_cus(), (nq + per_wg - 1) / per_wg);
+  return clamp_grid((nq + per_wg - 1) / per_wg, (nq + per_wg - 1) / per_wg);
 }
 
 // Decode: one wave per whole slice of kSliceQuarters quarters, then one wave
@@ -272,12 +272,20 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const uint32_t* a
 // Both passes.  When q_out has room (8 nb bytes against head_bytes: from
 // about 1040 blocks up), pass 1 leaves per-workgroup maxima and cleared counters at
 // the head of q_out (which pass 2 overwrites last), so no word has to be
-// zeroed first; smaller tensors take the zeroed-word path.
+// zeroed first; smaller tensors take the zeroed-word path.  So do row-major
+// inputs of kOneShotInputBytes and more: with the amax in one word, pass 2
+// runs a workgroup per chunk, which streams inputs well past the last-level
+// cache faster than the persistent grid that the per-workgroup maxima call
+// for (bf16, 14336 columns, step with the zeroing kernel included: 470 MB
+// input even, 587 MB 2.5% faster, 705 MB 3.3%, 939 MB 5.5%; below about
+// 470 MB the persistent grid's cache reuse wins, 268 MB by 7%).
 template <typename T, typename SMAP = RowMajorScales>
 nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_t* s, float* g,
                           float* amax, hipStream_t st, SMAP smap = SMAP{}) {
   const int g1 = amax_grid_for(x, nb);
-  if (nb == 0 || head_bytes(g1) > 8 * nb || env_int("NVFP4RQ_ZEROED_AMAX")) {
+  const bool large = std::is_same_v<SMAP, RowMajorScales> &&
+                     nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
+  if (nb == 0 || head_bytes(g1) > 8 * nb || large || env_int("NVFP4RQ_ZEROED_AMAX")) {
     nvfp4_status r = enqueue_rotamax(x, nb, rotate, amax, st);
     if (r != NVFP4_OK) return r;
     return enqueue_quant(x, nb, rotate, reinterpret_cast<const uint32_t*>(amax), 0, amax, q, s, g, st,

@@ -523,6 +523,26 @@ def test_timed_entry_point(nv):
             assert 0.0 < ms < 100.0, (k, ms)
 
 
+def test_large_input_path(nv):
+    """From 512 MiB of input the fused call hands the amax over through a
+    zeroed word (three kernels) and pass 2 runs a workgroup per chunk, the
+    first workgroups taking the last chunks; just below that size it keeps
+    the two-kernel path.  Both match the oracle byte for byte."""
+    x = mixed_input(16384, 16384, "bf16", seed=77)
+    for cols, want in ((16384, 3), (16368, 2)):
+        xs = np.ascontiguousarray(x[:, :cols])
+        xd = to_dev(xs)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in ev:
+            e.record()
+        torch.cuda.synchronize()
+        q, s, g, a, nk = nv.rotquant_timed(xd, ev)
+        torch.cuda.synchronize()
+        assert nk == want, (cols, nk)
+        compare(f"16384x{cols} bf16", xs, True, (q, s, g, a))
+        del xd, q, s
+
+
 # ---------------------------------------------------------------- beyond 2^31 elements
 
 def test_beyond_two_to_the_31_elements(nv):

@@ -316,6 +316,13 @@ def main() -> int:
     sw = torch.empty(nv.swizzled_scale_bytes(ROWS, COLS), dtype=torch.uint8, device=dev)
     sw_ms = timed(lambda: nv.rotquant_swizzled(x, rotate=ROTATE, out=(qu, sw, gu, au)))
 
+    # Calibration: the same launch sequence with no-arithmetic twins of the two
+    # kernels (same grids, access patterns, non-temporal rule, chunk order and
+    # bytes), timed like the step: the ceiling this byte mix reaches here.
+    qc, sc = torch.empty_like(q), torch.empty_like(s)
+    calib_ms = timed(lambda: nv.stream_calibrate(x, out=(qc, sc)))
+    del qc, sc
+
     # Context: decode (codes + scales + g in, fp32 out, inverse rotation).
     yd = nv.dequant(q, s, g, rotate=ROTATE)
     dq_ms = timed(lambda: nv.dequant(q, s, g, rotate=ROTATE, out=yd))
@@ -365,6 +372,11 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": nbytes["pass2"],
                      "duration": "mean of HIP events recorded at the kernel's own start and end "
                                  "inside the fused call (hipExtLaunchKernel)"},
+        "calibration": {"kind": "no-arithmetic twins of both kernels: same grids, access patterns "
+                                "and bytes (nvfp4_stream_calibrate)",
+                        "ms": round(calib_ms, 5),
+                        "gbs": round(nbytes["step"] / (calib_ms * 1e-3) / 1e9, 2),
+                        "value_over_calibration": round(calib_ms / ms, 4)},
         "mxfp4_single_pass": {"ms": round(mx_ms, 5), "bytes_per_elem": mx_bytes / n,
                               "gbs": round(mx_bytes / (mx_ms * 1e-3) / 1e9, 2)},
         "unfused_three_kernel": {"ms": round(unfused_ms, 5),

@@ -164,8 +164,8 @@ nvfp4_status nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *gsca
  *             timed.
  *   nkernels  receives the number of kernels launched: 2 (amax pass,
  *             quantize pass) when q_out has room for pass 1's partial maxima,
- *             3 (zeroing, amax, quantize) for small tensors, 1 or 2 for
- *             empty ones.
+ *             3 (zeroing, amax, quantize) for small tensors and for inputs of
+ *             512 MiB and more, 1 or 2 for empty ones.
  * Results are those of nvfp4_rotquant (nvfp4_rotquant_f32 for the _f32
  * variant).  NVFP4_ERR_NULL when events or nkernels is NULL or npairs < 1.
  */
@@ -254,6 +254,23 @@ nvfp4_status mxfp4_dequant(const uint8_t *q, const uint8_t *s, int64_t rows, int
                            int rotate, float *y_out, hipStream_t stream);
 
 /* Static English text for a status code; never NULL. */
+/*
+ * Measurement support, not part of the method: the launch sequence of
+ * nvfp4_rotquant (or _f32) for the same tensor, with each pass replaced by a
+ * twin kernel that has the same grid, wave layout, load and store widths,
+ * non-temporal rule and chunk order, and does no arithmetic beyond a bitwise
+ * fold of the loaded words.  Timing it gives the ceiling the fused call's
+ * byte mix (2 B read, then 2 B read and 0.5625 B written per bf16 element)
+ * can reach on the machine at hand.
+ *   x, rows, cols, q_out, s_out  as for nvfp4_rotquant; q_out and s_out
+ *   receive meaningless bytes.
+ * Errors as for nvfp4_rotquant.
+ */
+nvfp4_status nvfp4_stream_calibrate(const uint16_t *x_bf16, int64_t rows, int64_t cols,
+                                    uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
+nvfp4_status nvfp4_stream_calibrate_f32(const float *x, int64_t rows, int64_t cols,
+                                        uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
+
 const char *nvfp4_status_string(nvfp4_status status);
 
 #ifdef __cplusplus

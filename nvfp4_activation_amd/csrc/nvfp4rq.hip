@@ -42,6 +42,7 @@
 #include "pass2.hpp"
 #include "mxfp4.hpp"
 #include "elementwise.hpp"
+#include "calibrate.hpp"
 
 namespace nvfp4rq {
 namespace {
@@ -202,6 +203,14 @@ nvfp4_status validate_quant(const T* x, int64_t rows, int64_t cols, int rotate, 
 int amax_grid_for(const uint16_t*, int64_t nb) { return amax_grid(nb, true); }
 int amax_grid_for(const float*, int64_t nb) { return amax_grid(nb, false); }
 
+// First 16-byte piece of a bf16 input that pass 1 reads with ordinary loads
+// (see launch_rotamax).
+int64_t bf16_nt_end(int64_t nb) {
+  const int64_t keep_mb = env_int("NVFP4RQ_LLC_KEEP_MB");
+  const int64_t keep_pieces = (keep_mb ? keep_mb << 20 : kLastLevelKeep) / 16;
+  return 2 * nb > keep_pieces ? 2 * nb - keep_pieces : 0;
+}
+
 hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* bits, int partials,
                           hipStream_t st) {
   const dim3 grid(amax_grid(nb, true));
@@ -212,9 +221,7 @@ hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* b
   // (step, keeping 96 / 128 / 144 / 176 / 240 MB): 103.5 / 101.0 / 100.9 /
   // 101.0 / 102.5 us; streaming less leaves pass 1 slower, streaming more
   // costs pass 2 its cache hits.  At 32768 x 14336 the rule takes 12 us off.
-  const int64_t keep_mb = env_int("NVFP4RQ_LLC_KEEP_MB");
-  const int64_t keep_pieces = (keep_mb ? keep_mb << 20 : kLastLevelKeep) / 16;
-  const int64_t nt_end = 2 * nb > keep_pieces ? 2 * nb - keep_pieces : 0;
+  const int64_t nt_end = bf16_nt_end(nb);
   return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials, nt_end)
                 : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials,
                          nt_end);
@@ -269,6 +276,10 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const uint32_t* a
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+bool zeroed_word_path(int g1, int64_t nb, bool large) {
+  return head_bytes(g1) > 8 * nb || large || env_int("NVFP4RQ_ZEROED_AMAX");
+}
+
 // Both passes.  When q_out has room (8 nb bytes against head_bytes: from
 // about 1040 blocks up), pass 1 leaves per-workgroup maxima and cleared counters at
 // the head of q_out (which pass 2 overwrites last), so no word has to be
@@ -285,7 +296,7 @@ nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_
   const int g1 = amax_grid_for(x, nb);
   const bool large = std::is_same_v<SMAP, RowMajorScales> &&
                      nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
-  if (nb == 0 || head_bytes(g1) > 8 * nb || large || env_int("NVFP4RQ_ZEROED_AMAX")) {
+  if (nb == 0 || zeroed_word_path(g1, nb, large)) {
     nvfp4_status r = enqueue_rotamax(x, nb, rotate, amax, st);
     if (r != NVFP4_OK) return r;
     return enqueue_quant(x, nb, rotate, reinterpret_cast<const uint32_t*>(amax), 0, amax, q, s, g, st,
@@ -294,6 +305,53 @@ nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_
   uint32_t* head = reinterpret_cast<uint32_t*>(q);
   if (launch_rotamax(x, nb, rotate, head, 1, st) != hipSuccess) return NVFP4_ERR_HIP;
   return enqueue_quant(x, nb, rotate, head, g1, amax, q, s, g, st, smap);
+}
+
+// Measurement support (calibrate.hpp): the fused call's launch sequence for
+// row-major scales, with the twins in place of the two passes.
+hipError_t launch_stream_read(const uint16_t* x, int64_t nb, uint32_t* out, int partials,
+                              hipStream_t st) {
+  return launch(stream_read_bf16_kernel, dim3(amax_grid(nb, true)), dim3(kThreads), st, x, nb, out,
+                partials, bf16_nt_end(nb));
+}
+hipError_t launch_stream_read(const float* x, int64_t nb, uint32_t* out, int partials,
+                              hipStream_t st) {
+  return launch(stream_read_f32_kernel, dim3(amax_grid(nb, false)), dim3(kThreads), st, x, nb, out,
+                partials);
+}
+
+template <typename T>
+nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                              hipStream_t st) {
+  int64_t nb = 0;
+  nvfp4_status r = check_shape(rows, cols, &nb);
+  if (r != NVFP4_OK) return r;
+  const int64_t n = rows * cols;
+  if (n != 0 && (!x || !q || !s)) return NVFP4_ERR_NULL;
+  if (n != 0 && (!aligned(x, 16) || !aligned(q, 16))) return NVFP4_ERR_ALIGN;
+  const Range rx = range_of(x, n * static_cast<int64_t>(sizeof(T)));
+  const Range rq = range_of(q, n / 2), rs = range_of(s, n / 16);
+  if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return NVFP4_ERR_ARG;
+  if (nb == 0) return NVFP4_OK;
+  const int g1 = amax_grid_for(x, nb);
+  const bool large = nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
+  uint32_t* word = reinterpret_cast<uint32_t*>(q);
+  RowMajorScales smap{};
+  const int64_t nchunks = smap.chunks(nb);
+  dim3 grid(quant_grid(nchunks * kThreads));
+  if (zeroed_word_path(g1, nb, large)) {
+    if (launch(zero_word_kernel, dim3(1), dim3(1), st, word) != hipSuccess) return NVFP4_ERR_HIP;
+    if (launch_stream_read(x, nb, word, 0, st) != hipSuccess) return NVFP4_ERR_HIP;
+    grid = dim3(clamp_grid(nchunks, nchunks));
+    smap.mirror = 1;
+  } else {
+    if (launch_stream_read(x, nb, word, 1, st) != hipSuccess) return NVFP4_ERR_HIP;
+    if constexpr (sizeof(T) == 2)
+      smap.xcd_order = nchunks % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
+  }
+  return launch(stream_rw_kernel<T>, grid, dim3(kThreads), st, x, nb, q, s, smap) == hipSuccess
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
 }
 
 // Size of the swizzled scale buffer for a [rows, cols] tensor; -1 for a bad
@@ -559,6 +617,16 @@ nvfp4_status mxfp4_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int
   const float* no_gscale = nullptr;
   return rotate ? launch_decode<true>(q, s, no_gscale, nq, y_out, Mxfp4Scales{}, stream)
                 : launch_decode<false>(q, s, no_gscale, nq, y_out, Mxfp4Scales{}, stream);
+}
+
+nvfp4_status nvfp4_stream_calibrate(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                                    uint8_t* q_out, uint8_t* s_out, hipStream_t stream) {
+  return stream_calibrate(x_bf16, rows, cols, q_out, s_out, stream);
+}
+
+nvfp4_status nvfp4_stream_calibrate_f32(const float* x, int64_t rows, int64_t cols, uint8_t* q_out,
+                                        uint8_t* s_out, hipStream_t stream) {
+  return stream_calibrate(x, rows, cols, q_out, s_out, stream);
 }
 
 const char* nvfp4_status_string(nvfp4_status status) {

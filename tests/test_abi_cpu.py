@@ -45,6 +45,8 @@ def lib():
         getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p, p, i, p]
     lib.nvfp4_swizzled_scale_bytes.argtypes = [i64, i64]
     lib.nvfp4_swizzled_scale_bytes.restype = i64
+    for name in ("nvfp4_stream_calibrate", "nvfp4_stream_calibrate_f32"):
+        getattr(lib, name).argtypes = [p, i64, i64, p, p, p]
     lib.nvfp4_status_string.argtypes = [i]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     return lib
@@ -58,7 +60,8 @@ def test_header_declares_the_boundary():
                  "nvfp4_rotate16", "nvfp4_rotate16_f32", "nvfp4_rotquant_swizzled",
                  "nvfp4_rotquant_swizzled_f32", "nvfp4_dequant_swizzled",
                  "nvfp4_swizzled_scale_bytes", "nvfp4_rotquant_timed",
-                 "nvfp4_rotquant_f32_timed"):
+                 "nvfp4_rotquant_f32_timed", "nvfp4_stream_calibrate",
+                 "nvfp4_stream_calibrate_f32"):
         assert must in names
 
 
@@ -128,6 +131,21 @@ def test_rotamax_validation(lib):
     assert f(X + 4, 4, 64, 1, A, None) == ERR_ALIGN
     assert f(X, 4, 64, 1, A + 2, None) == ERR_ALIGN
     assert f(X, 4, 64, 1, X + 64, None) == ERR_ARG
+
+
+def test_stream_calibrate_validation(lib):
+    for name in ("nvfp4_stream_calibrate", "nvfp4_stream_calibrate_f32"):
+        f = getattr(lib, name)
+        assert f(None, 4, 64, Q, S, None) == ERR_NULL
+        assert f(X, 4, 64, None, S, None) == ERR_NULL
+        assert f(X, 4, 64, Q, None, None) == ERR_NULL
+        assert f(X, 4, 40, Q, S, None) == ERR_SHAPE
+        assert f(X, -1, 64, Q, S, None) == ERR_SHAPE
+        assert f(X + 8, 4, 64, Q, S, None) == ERR_ALIGN
+        assert f(X, 4, 64, Q + 8, S, None) == ERR_ALIGN
+        assert f(X, 4, 64, X, S, None) == ERR_ARG
+        assert f(X, 4, 64, Q, Q + 16, None) == ERR_ARG
+        assert f(None, 0, 64, None, None, None) == OK
 
 
 def test_dequant_validation(lib):

@@ -76,6 +76,19 @@ def load_traffic(n_elem: int):
     return d.get("pass2_hbm_bytes")
 
 
+def load_valu():
+    """VALU lane-instructions per element of each pass (rocprofv3 SQ_INSTS_VALU
+    x 64 / elements) from the committed counter summary; None when it is
+    missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "rotquant_t3_lognormal_16384x8192_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_sha") != kernel_source_sha() or "valu_per_element" not in d:
+        return None
+    return d["valu_per_element"]
+
+
 def cpu_baseline(x_np, rotate: bool, label: str) -> dict:
     """The oracle, untuned, on this host's cores: both passes over the whole
     tensor, repeated for about ten seconds (at least three runs), median run.
@@ -335,6 +348,7 @@ def main() -> int:
     same = bool(torch.equal(q, q2) and torch.equal(s, s2) and torch.equal(g, g2))
 
     traffic = load_traffic(n) if WORKLOAD == DEFAULT_WORKLOAD else None
+    valu = load_valu() if WORKLOAD == DEFAULT_WORKLOAD else None
     out = {
         "metric": f"rotate+NVFP4-quantize GB/s and % of HBM peak, {ROWS}x{COLS} {dname}, 1 GPU",
         "value": round(gbs, 2),
@@ -369,6 +383,9 @@ def main() -> int:
                      "achieved": round(p2_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(p2_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     # VALU lane-instructions per element (SQ_INSTS_VALU x 64 / n);
+                     # the quantize pass could issue 12.6 at the 8 TB/s element rate
+                     "valu_per_element": valu,
                      "algorithmic_bytes_per_launch": nbytes["pass2"],
                      "duration": "mean of HIP events recorded at the kernel's own start and end "
                                  "inside the fused call (hipExtLaunchKernel)"},

@@ -19,9 +19,9 @@ namespace {  // one translation unit (nvfp4rq.hip): internal linkage
 // quarters per iteration, lane l quarters l, l + 64, ..., so that every store
 // instruction of the wave writes 1 KiB of consecutive outputs.  A block's four
 // quarters sit in the four lanes of a quad; strides 1 and 2 of the butterfly
-// run in lane, strides 4 and 8 through quad lane exchanges.  The tail
-// iteration is wave-uniform and every lane runs the exchanges; only the loads
-// and stores are predicated.
+// run in lane, strides 4 and 8 through quad lane exchanges, so every lane of
+// a quad runs them, in partial iterations too (only loads and stores are
+// predicated there).
 constexpr int kQuarters = 8;
 
 __device__ __forceinline__ void load_quarter(const float* __restrict__ x, int64_t pc, float z[4]) {
@@ -41,11 +41,11 @@ __device__ __forceinline__ void load_quarter(const uint16_t* __restrict__ x, int
 // quarters (2048 outputs) and launch one wave per slice.  A wave stages its
 // slice's codes (1 KiB: two 8-byte loads per lane) and, for row-major scales,
 // its scale bytes (one or two byte loads per lane) in its own part of LDS, and
-// reads them back in the quarter layout.  At 16384 x 8192 this runs the
-// rotated decode in 90 us where per-quarter code and scale loads in a grid of
-// 8 persistent workgroups per CU took 123 us: the 512 MiB of fp32 stores run
-// at the chip's write rate only when the few reads between them are issued
-// early, as few wide loads, by waves that do not come back for more.
+// reads them back in the quarter layout.  Rotated decode at 16384 x 8192,
+// event-timed around the kernel: 90 us like this; 109 us with per-quarter
+// code and scale loads and one wave per slice; 124 us with per-quarter loads
+// in a grid of 8 persistent workgroups per CU; the 512 MiB of fp32 stores
+// alone, 79 us.
 constexpr int64_t kSliceQuarters = 64 * kQuarters;
 
 // Where a decode kernel finds the scale of a quarter and what a scale byte

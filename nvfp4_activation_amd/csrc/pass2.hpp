@@ -181,11 +181,9 @@ __device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, 
     f->load(x, b);
 }
 
-// Pass 2 body: each lane rotates, scales and encodes one block per iteration.
-// Workgroup w handles the chunks w, w + G, w + 2G, ... of its scale-layout
-// policy (G = grid size), last chunk first: the chunks pass 1 read last are
-// the likeliest to still be in the last-level cache.  Every step is the definition of section 2
-// (hadamard_nvfp4_kernel) in binary32:
+// One block of pass 2, in one lane: rotation (in place on lo, hi), the block
+// scale byte and the two words of E2M1 codes.  Every step is the definition
+// of section 2 (hadamard_nvfp4_kernel) in binary32:
 //   z     = S16 x                         (butterfly, no scaling yet)
 //   a_b   = max |y| = 0.25 max |z|        (exact for any rounding, see pass 1)
 //   v     = (a_b / 6) / g,  s = E4M3(min(v, 448))
@@ -195,106 +193,149 @@ __device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, 
 // 4 are exact there), the divisions are corrected reciprocal products and the
 // per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
 // Otherwise every division is a true binary32 division.
+template <bool ROTATE, bool FAST>
+__device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, float rg,
+                                             const float2* __restrict__ tab, uint32_t* sb_out,
+                                             u32x2* w_out) {
+  if (ROTATE) {
+    stages_1_2_4(lo);
+    stages_1_2_4(hi);
+    stage_8(lo, hi);
+  }
+  float az = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
+  uint32_t sb;
+  if (FAST) {
+    const float ab = ROTATE ? 0.25f * az : az;
+    const float a6 = div_corrected(ab, 6.0f, kRecip6);
+    // A quotient too large for binary32 makes the product NaN; fminf keeps
+    // 448, the right byte for any block value that large.
+    sb = e4m3_byte(div_corrected(a6, g, rg));
+    const float2 t = tab[sb];
+    if (az <= kQuotientLimit * t.x) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = div_corrected(lo[i], t.x, t.y);
+        hi[i] = div_corrected(hi[i], t.x, t.y);
+      }
+    } else {
+      // Only with a global scale from elsewhere (the amax of an earlier
+      // step) can a block's quotients approach the binary32 range; divide
+      // exactly (y = z / 4 and d = 4d / 4 are exact here).
+      const float d = ROTATE ? 0.25f * t.x : t.x;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
+        hi[i] = (ROTATE ? 0.25f * hi[i] : hi[i]) / d + 0.0f;
+      }
+    }
+  } else {
+    if (ROTATE) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = 0.25f * lo[i];
+        hi[i] = 0.25f * hi[i];
+      }
+    }
+    const float ab = ROTATE ? 0.25f * az : az;
+    sb = e4m3_byte((ab / 6.0f) / g);
+    const float sf = e4m3_value(sb) * g;
+    const float d = sf == 0.0f ? 1.0f : sf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = lo[i] / d + 0.0f;
+      hi[i] = hi[i] / d + 0.0f;
+    }
+  }
+  *sb_out = sb;
+  *w_out = u32x2{e2m1_pack8(lo), e2m1_pack8(hi)};
+}
+
+// Pass 2 over row-major chunks (256 consecutive blocks, a block per lane).
+// Workgroup w handles the chunks w, w + G, w + 2G, ... (G = grid size), last
+// chunk first: the chunks pass 1 read last are the likeliest to still be in
+// the last-level cache.  The first chunk's blocks were loaded before the
+// prologue, so its iteration is peeled off.
+template <typename T, bool ROTATE, bool FAST>
+__device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t nb, float g,
+                                                const float2* __restrict__ tab,
+                                                uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                RowMajorScales smap, const HeadGuard& head,
+                                                const FirstBlock<T>& first) {
+  const int64_t nchunks = smap.chunks(nb);
+  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const float rg = FAST ? 1.0f / g : 0.0f;
+  auto finish = [&](int64_t chunk, float lo[8], float hi[8]) {
+    uint32_t sb;
+    u32x2 w;
+    encode_block<ROTATE, FAST>(lo, hi, g, rg, tab, &sb, &w);
+    // Codes are stored non-temporally: nothing reads them back here, and in
+    // the last-level cache they would only displace input that this pass
+    // re-reads (16384 x 8192: 1.6 us off the step; 32768 x 14336: 4.8 us).
+    u32x2* qc = reinterpret_cast<u32x2*>(q) + chunk * kThreads;
+    __builtin_nontemporal_store(w, qc + threadIdx.x);
+    (s + chunk * kThreads)[threadIdx.x] = static_cast<uint8_t>(sb);
+  };
+  if (mine <= 0) return;
+  {
+    const int64_t chunk = smap.order((mine - 1) * gridDim.x + blockIdx.x, nchunks);
+    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
+    if (chunk * kThreads + threadIdx.x < nb) {
+      float lo[8], hi[8];
+      first.unpack(lo, hi);
+      finish(chunk, lo, hi);
+    }
+  }
+  for (int64_t it = mine - 2; it >= 0; --it) {
+    const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
+    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
+    if (chunk * kThreads + threadIdx.x < nb) {
+      float lo[8], hi[8];
+      load_block(x + chunk * kThreads * 16, threadIdx.x, lo, hi);
+      finish(chunk, lo, hi);
+    }
+  }
+}
+
+// Pass 2 over swizzled chunks (see SwizzledScales), in the same order; the
+// chunk's scale tiles are assembled in LDS and stored whole.
 template <typename T, bool ROTATE, bool FAST, typename SMAP>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
                                              const float2* __restrict__ tab,
                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                             SMAP smap, const HeadGuard& head,
-                                             const FirstBlock<T>& first) {
+                                             SMAP smap, const HeadGuard& head) {
   const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
-  __shared__ uint32_t stage[SMAP::kStaged ? 512 : 1];  // 4 scale tiles
+  __shared__ uint32_t stage[512];  // 4 scale tiles
   for (int64_t it = mine - 1; it >= 0; --it) {
     const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
     if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
-    if constexpr (SMAP::kStaged) {
-      for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
-      __syncthreads();
-    }
+    for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
+    __syncthreads();
 #pragma unroll 1
     for (int sub = 0; sub < SMAP::kSub; ++sub) {
       int64_t b, si;
       if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
       float lo[8], hi[8];
-      if (!SMAP::kStaged && it == mine - 1 && sub == 0) {  // loaded before the prologue
-        first.unpack(lo, hi);
-      } else {
-        load_block(x, b, lo, hi);
-      }
-      if (ROTATE) {
-        stages_1_2_4(lo);
-        stages_1_2_4(hi);
-        stage_8(lo, hi);
-      }
-      float az = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
+      load_block(x, b, lo, hi);
       uint32_t sb;
-      if (FAST) {
-        const float ab = ROTATE ? 0.25f * az : az;
-        const float a6 = div_corrected(ab, 6.0f, kRecip6);
-        // A quotient too large for binary32 makes the product NaN; fminf keeps
-        // 448, the right byte for any block value that large.
-        sb = e4m3_byte(div_corrected(a6, g, rg));
-        const float2 t = tab[sb];
-        if (az <= kQuotientLimit * t.x) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            lo[i] = div_corrected(lo[i], t.x, t.y);
-            hi[i] = div_corrected(hi[i], t.x, t.y);
-          }
-        } else {
-          // Only with a global scale from elsewhere (the amax of an earlier
-          // step) can a block's quotients approach the binary32 range; divide
-          // exactly (y = z / 4 and d = 4d / 4 are exact here).
-          const float d = ROTATE ? 0.25f * t.x : t.x;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
-            hi[i] = (ROTATE ? 0.25f * hi[i] : hi[i]) / d + 0.0f;
-          }
-        }
-      } else {
-        if (ROTATE) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            lo[i] = 0.25f * lo[i];
-            hi[i] = 0.25f * hi[i];
-          }
-        }
-        const float ab = ROTATE ? 0.25f * az : az;
-        sb = e4m3_byte((ab / 6.0f) / g);
-        const float sf = e4m3_value(sb) * g;
-        const float d = sf == 0.0f ? 1.0f : sf;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lo[i] = lo[i] / d + 0.0f;
-          hi[i] = hi[i] / d + 0.0f;
-        }
-      }
-      // Codes are stored non-temporally: nothing reads them back here, and in
-      // the last-level cache they would only displace input that this pass
-      // re-reads (16384 x 8192: 1.6 us off the step; 32768 x 14336: 4.8 us).
-      const u32x2 w = {e2m1_pack8(lo), e2m1_pack8(hi)};
+      u32x2 w;
+      encode_block<ROTATE, FAST>(lo, hi, g, rg, tab, &sb, &w);
       __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(q + b * 8));
-      if constexpr (SMAP::kStaged)
-        reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
-      else
-        s[si] = static_cast<uint8_t>(sb);
+      reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
     }
-    if constexpr (SMAP::kStaged) {
-      // whole tiles, padding zeros included, in one coalesced store
-      __syncthreads();
-      int64_t first;
-      int ntiles;
-      smap.chunk_tiles(chunk, &first, &ntiles);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
-      for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
-        dst[i] = stage[i];
-      __syncthreads();
-    }
+    // whole tiles, padding zeros included, in one coalesced store
+    __syncthreads();
+    int64_t first;
+    int ntiles;
+    smap.chunk_tiles(chunk, &first, &ntiles);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
+    for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
+      dst[i] = stage[i];
+    __syncthreads();
   }
 }
 
@@ -345,11 +386,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         tab[threadIdx.x] = make_float2(d, 1.0f / d);
       }
       __syncthreads();
-      quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head, first);
+      if constexpr (SMAP::kStaged)
+        quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head);
+      else
+        quant_blocks_rm<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head, first);
       return;
     }
   }
-  quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head, first);
+  if constexpr (SMAP::kStaged)
+    quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head);
+  else
+    quant_blocks_rm<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head, first);
 }
 
 }  // namespace

@@ -61,9 +61,19 @@ struct SwizzledScales {
   static constexpr bool kStaged = true;  // scale tiles assembled in LDS
   int64_t rows;
   uint32_t cb, ctiles, cs;  // blocks per row, ceil(cb / 4), ceil(cb / 16)
-  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const {
+  int mirror;               // as RowMajorScales::mirror
+  // A chunk's row tile and 16-block column, divided out once per chunk (a
+  // 64-bit division per sub-iteration cost 135 scalar instructions each).
+  struct Tile {
+    int64_t rt;
+    uint32_t cw;
+  };
+  __device__ __forceinline__ Tile split(int64_t chunk) const {
     const int64_t rt = chunk / cs;
-    return (rt * 128 * cb + (chunk - rt * cs) * 16) * 8;
+    return Tile{rt, static_cast<uint32_t>(chunk - rt * cs)};
+  }
+  __device__ __forceinline__ int64_t first_q_byte(Tile t) const {
+    return (t.rt * 128 * cb + static_cast<int64_t>(t.cw) * 16) * 8;
   }
   __device__ __forceinline__ static int64_t place(uint32_t r, uint32_t c, uint32_t ctiles) {
     const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
@@ -75,21 +85,21 @@ struct SwizzledScales {
     return place(r, bb - r * cb, ctiles);
   }
   __host__ __device__ int64_t chunks(int64_t) const { return ((rows + 127) / 128) * cs; }
-  __device__ __forceinline__ int64_t order(int64_t i, int64_t) const { return i; }
-  __device__ __forceinline__ bool locate(int64_t chunk, int sub, uint32_t tid, int64_t, int64_t* b,
-                                         int64_t* si) const {
-    const int64_t rt = chunk / cs;
-    const uint32_t r = static_cast<uint32_t>(rt * 128 + sub * 16 + (tid >> 4));
-    const uint32_t c = static_cast<uint32_t>(chunk - rt * cs) * 16 + (tid & 15u);
+  __device__ __forceinline__ int64_t order(int64_t i, int64_t nchunks) const {
+    return mirror ? nchunks - 1 - i : i;
+  }
+  __device__ __forceinline__ bool locate(Tile t, int sub, uint32_t tid, int64_t* b, int64_t* si) const {
+    const uint32_t r = static_cast<uint32_t>(t.rt * 128 + sub * 16 + (tid >> 4));
+    const uint32_t c = t.cw * 16 + (tid & 15u);
     if (r >= rows || c >= cb) return false;
     *b = static_cast<int64_t>(r) * cb + c;
     *si = place(r & 127u, c & 15u, 4);  // byte within the chunk's tiles
     return true;
   }
-  // The chunk's tiles (rt, 4 c16 .. 4 c16 + 3) are consecutive in memory.
-  __device__ __forceinline__ void chunk_tiles(int64_t chunk, int64_t* first_byte, int* ntiles) const {
-    const int64_t rt = chunk / cs, ct0 = (chunk - rt * cs) * 4;
-    *first_byte = (rt * ctiles + ct0) * 512;
+  // The chunk's tiles (rt, 4 cw .. 4 cw + 3) are consecutive in memory.
+  __device__ __forceinline__ void chunk_tiles(Tile t, int64_t* first_byte, int* ntiles) const {
+    const int64_t ct0 = static_cast<int64_t>(t.cw) * 4;
+    *first_byte = (t.rt * ctiles + ct0) * 512;
     *ntiles = static_cast<int>(ctiles - ct0 < 4 ? ctiles - ct0 : 4);
   }
 };
@@ -311,14 +321,14 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
   const float rg = FAST ? 1.0f / g : 0.0f;
   __shared__ uint32_t stage[512];  // 4 scale tiles
   for (int64_t it = mine - 1; it >= 0; --it) {
-    const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
-    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
+    const auto tile = smap.split(smap.order(it * gridDim.x + blockIdx.x, nchunks));
+    if (head.counters && smap.first_q_byte(tile) < head.bytes) wait_for_head(head);
     for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
     __syncthreads();
 #pragma unroll 1
     for (int sub = 0; sub < SMAP::kSub; ++sub) {
       int64_t b, si;
-      if (!smap.locate(chunk, sub, threadIdx.x, nb, &b, &si)) continue;
+      if (!smap.locate(tile, sub, threadIdx.x, &b, &si)) continue;
       float lo[8], hi[8];
       load_block(x, b, lo, hi);
       uint32_t sb;
@@ -331,7 +341,7 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
     __syncthreads();
     int64_t first;
     int ntiles;
-    smap.chunk_tiles(chunk, &first, &ntiles);
+    smap.chunk_tiles(tile, &first, &ntiles);
     uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
     for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
       dst[i] = stage[i];

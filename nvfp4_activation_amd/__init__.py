@@ -104,9 +104,11 @@ def _variant(x: torch.Tensor, base: str) -> str:
     raise TypeError(f"input must be bfloat16 or float32, got {x.dtype}")
 
 
-def _check_input(x: torch.Tensor) -> tuple[int, int]:
+def _check_input(x: torch.Tensor, multiple: int = 16) -> tuple[int, int]:
     if x.dim() != 2:
         raise ValueError("input must be 2-D [rows, cols]")
+    if x.shape[1] % multiple:
+        raise ValueError(f"cols must be a multiple of {multiple}, got {x.shape[1]}")
     if not x.is_cuda:
         raise ValueError("input must be a device tensor")
     if not x.is_contiguous():
@@ -298,7 +300,7 @@ def rotate16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> t
 def mx_rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, stream=None):
     """MXFP4 single pass.  x: bfloat16 or float32 [rows, cols], cols % 32 == 0.
     Returns (q uint8 [rows, cols/2], s uint8 [rows, cols/32] E8M0 bytes)."""
-    rows, cols = _check_input(x)
+    rows, cols = _check_input(x, 32)
     if out is None:
         q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
         s = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)

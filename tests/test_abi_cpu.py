@@ -298,3 +298,15 @@ def test_binding_buffer_checks_on_host():
         nv._buf(ok, 8, torch.uint8, torch.device("cuda", 0), "q")
     with pytest.raises(TypeError, match="tensor"):
         nv._buf(None, 8, torch.uint8, cpu, "q")
+
+
+def test_binding_rejects_ragged_columns_on_host():
+    """The binding names the column rule itself (before any device check)."""
+    import torch
+    import nvfp4_activation_amd as nv
+    with pytest.raises(ValueError, match="multiple of 16"):
+        nv.rotquant(torch.empty(4, 24, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="multiple of 32"):
+        nv.mx_rotquant(torch.empty(4, 48, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="device tensor"):
+        nv.rotquant(torch.empty(4, 32, dtype=torch.bfloat16))

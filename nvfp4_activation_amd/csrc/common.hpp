@@ -26,9 +26,9 @@ constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
 // true divisions.
 constexpr float kQuotientLimit = 0x1p100f;
 constexpr int64_t kLastLevelKeep = 144LL << 20;  // bytes of input pass 1 leaves cached
-// From this input size on, the two passes hand the amax over through a zeroed
-// word instead of per-workgroup maxima, so that pass 2 can run a workgroup per
-// chunk (see enqueue_both).
+// From this input size on, the two passes of a row-major call hand the amax
+// over through a zeroed word instead of per-workgroup maxima, so that pass 2
+// can run a workgroup per chunk (see enqueue_both).
 constexpr int64_t kOneShotInputBytes = 512LL << 20;
 // Arrival counters of the quantize pass when pass 1 leaves its partial maxima
 // in q_out: spread over kCounters words on separate 128-byte lines, since

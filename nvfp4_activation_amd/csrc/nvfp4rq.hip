@@ -120,17 +120,18 @@ int amax_grid(int64_t nb, bool bf16) {
   return clamp_grid(want, (nb + per_wg - 1) / per_wg);
 }
 
-// Pass 2: 8 workgroups per compute unit, one 256-block chunk per iteration.
+// Pass 2 when it first reduces pass 1's per-workgroup maxima: 8 workgroups
+// per compute unit, one 256-block chunk per iteration (with the amax as one
+// word, enqueue_quant launches a workgroup per chunk instead).
 int quant_grid(int64_t nb) {
   int64_t want = env_int("NVFP4RQ_QUANT_WGS");
   if (!want) want = 8LL * device_cus();
   return clamp_grid(want, (nb + kThreads - 1) / kThreads);
 }
 
-int generic_grid(int64_t nb) { return clamp_grid(8LL * device_cus(), (nb + kThreads - 1) / kThreads); }
-
 // Rotation alone: one workgroup per kThreads * kQuarters quarters (16384 x
-// 8192 bf16: 123 us against 128 with 8 persistent workgroups per CU).
+// 8192 bf16, kernel-only: 121 us against 124 with 8 persistent workgroups
+// per CU).
 int quarter_grid(int64_t nq) {
   const int64_t per_wg = static_cast<int64_t>(kThreads) * kQuarters;
   return clamp_grid((nq + per_wg - 1) / per_wg, (nq + per_wg - 1) / per_wg);

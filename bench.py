@@ -15,9 +15,11 @@ before every step (outside the events) a 1 GiB buffer is read, so the input is
 not resident in the 256 MB last-level cache or the L2s and no dirty lines are
 left to write back during the step (cold, clean cache).
 A second loop runs the same steps through the library's measurement hook,
-whose two kernels record HIP events at their own start and end: their
-intervals are the live durations of pass 1 and of pass 2 (the dominant
-kernel, used for the roofline figure).
+whose kernels record HIP events at their own start and end: the intervals of
+the last two are the live durations of pass 1 and of pass 2 (the dominant
+kernel, used for the roofline figure).  The same launch sequence with
+no-arithmetic twins of both kernels, timed like the step, gives the ceiling
+for this byte mix (`calibration`).
 
 Prints one JSON line (rank 0).  `--gpus N` with N > 1 exits: the benchmark
 measures one GPU.
@@ -212,7 +214,7 @@ def main() -> int:
     gbs = nbytes["step"] / (ms * 1e-3) / 1e9
 
     # Context: the same step replayed as a captured HIP graph (launch path of
-    # serving loops); the captured work is the identical two kernels.
+    # serving loops); the captured work is the identical kernels.
     graph_ms = None
     if args.graph:
         side = torch.cuda.Stream()

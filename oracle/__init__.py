@@ -75,6 +75,8 @@ def _load():
     lib.oracle_swizzle_scales.argtypes = [_ptr, _i64, _i64, _ptr]
     lib.oracle_rotate_tensor.argtypes = [_ptr, _int, _i64, _i64, _ptr, _int]
     lib.oracle_rotate_tensor.restype = _int
+    lib.oracle_rotate_matrix.argtypes = [_ptr, _int, _i64, _i64, _ptr, _ptr, _int]
+    lib.oracle_rotate_matrix.restype = _int
     lib.oracle_mx_dequant_f64.argtypes = [_ptr, _ptr, _i64, _i64, _int, _ptr, _int]
     lib.oracle_e4m3_byte_bits.argtypes = [_u32, _u32, _ptr, _int]
     _lib = lib
@@ -109,6 +111,20 @@ def rotate_tensor(x: np.ndarray, nthreads: int = 0) -> np.ndarray:
     rows, cols = x.shape
     y = np.empty((rows, cols), dtype=np.float32)
     if _load().oracle_rotate_tensor(_p(x), _is_f32(x), rows, cols, _p(y), nthreads):
+        raise ValueError("cols must be a multiple of 16")
+    return y
+
+
+def rotate_matrix(x: np.ndarray, r: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """y = x_b r for every 16-element block x_b of x [rows, cols] (r: 16 x 16,
+    rows are inputs), binary32 with the fused multiply-add order of
+    oracle_rotate_matrix; float32."""
+    rows, cols = x.shape
+    rr = np.ascontiguousarray(r, dtype=np.float32)
+    if rr.shape != (16, 16):
+        raise ValueError("r must be 16 x 16")
+    y = np.empty((rows, cols), dtype=np.float32)
+    if _load().oracle_rotate_matrix(_p(x), _is_f32(x), rows, cols, _p(rr), _p(y), nthreads):
         raise ValueError("cols must be a multiple of 16")
     return y
 

@@ -660,6 +660,41 @@ int oracle_rotate_tensor(const void *x, int is_f32, int64_t rows, int64_t cols, 
     return 0;
 }
 
+/*
+ * A general 16x16 block rotation (page "A Fused Hadamard + NVFP4
+ * Quantization Kernel in Triton", "Try this" item 3: the Hadamard replaced by
+ * a random orthogonal 16x16 matrix).  For each 16-element block x,
+ * y_j = sum_k x_k r[k][j] (r row-major, y = x r), in binary32 with this
+ * summation order, a reading the page leaves open (its tl.dot fixes none):
+ * acc = RN(x_0 r[0][j]), then acc = RN(x_k r[k][j] + acc) as one fused
+ * multiply-add for k = 1..15.  The same order on the GPU gives the same bits.
+ * Returns 0, or -1 on a bad shape.
+ */
+int oracle_rotate_matrix(const void *x, int is_f32, int64_t rows, int64_t cols,
+                         const float *r, float *y, int nthreads)
+{
+    if (cols % 16 != 0 || rows < 0 || cols < 0)
+        return -1;
+    int64_t nb = rows * (cols / 16);
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+#endif
+    for (int64_t b = 0; b < nb; b++) {
+        float xb[16];
+        load_span(x, is_f32, b * 16, 16, xb);
+        for (int j = 0; j < 16; j++) {
+            float acc = xb[0] * r[j];
+            for (int k = 1; k < 16; k++)
+                acc = fmaf(xb[k], r[16 * k + j], acc);
+            y[16 * b + j] = acc;
+        }
+    }
+    (void)nthreads;
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* Swizzled block-scale layout                                        */
 /* ------------------------------------------------------------------ */

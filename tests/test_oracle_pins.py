@@ -629,3 +629,82 @@ def test_swizzle_worked_positions():
     assert out[2 * 512] == 4                         # tile (1,0) starts the second tile row
     assert out[4 * 512 - 1] == 5                     # last byte of tile (1,1)
     assert out[512 + 16 * 8 + 4 * 1 + 0] == 6        # row 40: j=8, i=1; column 4: k=0
+
+
+# ---------------------------------------------------------------- general block rotation ("Try this" 3)
+
+def random_orthogonal16(seed: int) -> np.ndarray:
+    """Q of the QR factorisation of a seeded 16 x 16 Gaussian matrix (signs
+    fixed so that R has a positive diagonal), rounded to binary32."""
+    rng = np.random.default_rng(seed)
+    q, r = np.linalg.qr(rng.standard_normal((16, 16)))
+    return (q * np.sign(np.diag(r))).astype(np.float32)
+
+
+def test_rotate_matrix_identity_and_permutation():
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((5, 64)) * 1e3).astype(np.float32)
+    assert np.array_equal(oracle.rotate_matrix(x, np.eye(16, dtype=np.float32)), x)
+    perm = rng.permutation(16)
+    P = np.zeros((16, 16), dtype=np.float32)
+    P[perm, np.arange(16)] = 1.0          # y_j = x_perm[j]
+    want = x.reshape(-1, 16)[:, perm].reshape(5, 64)
+    assert np.array_equal(oracle.rotate_matrix(x, P), want)
+    xb = _bf16(x.astype(np.float64).reshape(-1)).reshape(5, 64)
+    assert np.array_equal(oracle.rotate_matrix(xb, np.eye(16, dtype=np.float32)), synth.bf16_to_f32(xb))
+
+
+def test_rotate_matrix_with_the_hadamard_equals_the_butterfly_when_exact():
+    """Small integers times +-1/4: every product and partial sum is exact in
+    either order, so the dense product equals the butterfly."""
+    rng = np.random.default_rng(32)
+    x = rng.integers(-1000, 1000, 6 * 48).astype(np.float32).reshape(6, 48)
+    H = sylvester16().astype(np.float32)      # entries +-1/4
+    assert np.array_equal(oracle.rotate_matrix(x, H), oracle.rotate_tensor(x))
+
+
+def test_rotate_matrix_follows_the_fused_multiply_add_order():
+    """Exact rational model of acc = RN(x0 r0j), acc = RN(xk rkj + acc):
+    bit for bit on random blocks and a random orthogonal matrix (a separately
+    rounded multiply and add, or another order, differs on such data)."""
+    rng = np.random.default_rng(33)
+    R = random_orthogonal16(5)
+    x = (rng.standard_normal((3, 16 * 8)) * np.exp2(rng.uniform(-20, 20, size=(3, 1)))).astype(np.float32)
+    got = oracle.rotate_matrix(x, R).reshape(-1, 16)
+    Rf = [[em.f32_to_frac(R[k, j]) for j in range(16)] for k in range(16)]
+    for bi, blk in enumerate(x.reshape(-1, 16)):
+        xf = [em.f32_to_frac(v) for v in blk]
+        for j in range(16):
+            acc = em.rn32(xf[0] * Rf[0][j])
+            for k in range(1, 16):
+                acc = em.rn32(xf[k] * Rf[k][j] + acc)
+            assert got[bi, j] == em.frac_to_f32(acc), (bi, j)
+    # the separately rounded variant really differs somewhere on this data
+    diff = 0
+    for bi, blk in enumerate(x.reshape(-1, 16)):
+        xf = [em.f32_to_frac(v) for v in blk]
+        for j in range(16):
+            acc = em.rn32(xf[0] * Rf[0][j])
+            for k in range(1, 16):
+                acc = em.rn32(em.rn32(xf[k] * Rf[k][j]) + acc)
+            diff += got[bi, j] != em.frac_to_f32(acc)
+    assert diff > 0
+
+
+def test_rotate_matrix_error_bound_and_round_trip():
+    """Against the fp64 product: |y - x R| <= gamma_16 sum_k |x_k r_kj|; and
+    rotating back with R^T returns x up to the same kind of bound (plus R's
+    own distance from orthogonality)."""
+    rng = np.random.default_rng(34)
+    R = random_orthogonal16(6)
+    x = (rng.standard_normal((40, 160)) * 3.0).astype(np.float32)
+    xb = x.reshape(-1, 16).astype(np.float64)
+    R64 = R.astype(np.float64)
+    y = oracle.rotate_matrix(x, R).reshape(-1, 16).astype(np.float64)
+    u = 2.0 ** -24
+    gamma = 16 * u / (1 - 16 * u)
+    assert np.all(np.abs(y - xb @ R64) <= gamma * (np.abs(xb) @ np.abs(R64)))
+    z = oracle.rotate_matrix(y.astype(np.float32).reshape(40, 160), np.ascontiguousarray(R.T))
+    orth = np.abs(R64 @ R64.T - np.eye(16)).max()
+    bound = (2 * gamma + 16 * orth) * (np.abs(xb) @ (np.abs(R64) @ np.abs(R64.T))) + 1e-30
+    assert np.all(np.abs(z.reshape(-1, 16) - xb) <= bound)

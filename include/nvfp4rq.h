@@ -225,6 +225,29 @@ nvfp4_status nvfp4_rotate16_f32(const float *x, int64_t rows, int64_t cols, floa
                                 hipStream_t stream);
 
 /*
+ * General block rotation: y = x R on every 16-element block, R a 16 x 16
+ * binary32 matrix given by the caller, stored as fp32 [rows, cols].  The page
+ * "A Fused Hadamard + NVFP4 Quantization Kernel in Triton" ("Try this" item 3)
+ * proposes replacing the Hadamard with a random orthogonal matrix and
+ * comparing the error; with nvfp4_rotquant_f32 (rotate = 0) on y and
+ * nvfp4_dequant (rotate = 0) followed by this call with R transposed, it runs
+ * that study on the GPU.  Arithmetic per output j of a block with inputs
+ * x_0 .. x_15: t = fl(x_0 * R[0][j]), then t = fma(x_k, R[k][j], t) for
+ * k = 1 .. 15 in that order; the result is t.
+ *   x      device, [rows, cols], 16-byte aligned, cols % 16 == 0.
+ *   r16    device, 256 floats, row-major (R[k][j] at r16[16 k + j]: row k
+ *          multiplies input k), 16-byte aligned; read only, may overlap x.
+ *   y_out  device fp32 [rows, cols], 16-byte aligned, overlapping neither x
+ *          nor r16.
+ * rows * cols == 0 returns NVFP4_OK and launches nothing (r16 must still be
+ * non-NULL and aligned).
+ */
+nvfp4_status nvfp4_rotate_matrix(const uint16_t *x_bf16, int64_t rows, int64_t cols,
+                                 const float *r16, float *y_out, hipStream_t stream);
+nvfp4_status nvfp4_rotate_matrix_f32(const float *x, int64_t rows, int64_t cols, const float *r16,
+                                     float *y_out, hipStream_t stream);
+
+/*
  * MXFP4 variant (page "A Fused Hadamard + NVFP4 Quantization Kernel in
  * Triton", section 1 contrasts NVFP4 with MXFP4: 32-element blocks,
  * power-of-two E8M0 scales; its "Try this" list asks for the error study under

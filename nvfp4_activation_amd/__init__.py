@@ -21,8 +21,8 @@ import torch
 __all__ = [
     "LIB_PATH", "Nvfp4Error", "rotquant", "rotamax", "quant_from_amax", "dequant",
     "status_string", "lib", "mx_rotquant", "mx_dequant",
-    "rotate16", "rotquant_timed", "rotquant_swizzled", "dequant_swizzled", "swizzled_scale_bytes",
-    "stream_calibrate",
+    "rotate16", "rotate_matrix", "rotquant_timed", "rotquant_swizzled", "dequant_swizzled",
+    "swizzled_scale_bytes", "stream_calibrate",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,12 +47,14 @@ _SIGS = {
     "nvfp4_quant_from_amax_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_dequant": [_p, _p, _p, _i64, _i64, _int, _p, _p],
     "nvfp4_rotate16": [_p, _i64, _i64, _p, _p],
+    "nvfp4_rotate_matrix": [_p, _i64, _i64, _p, _p, _p],
     "nvfp4_rotquant_swizzled": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_rotquant_timed": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p, _p, _int, _p],
     "nvfp4_rotquant_f32_timed": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p, _p, _int, _p],
     "nvfp4_rotquant_swizzled_f32": [_p, _i64, _i64, _int, _p, _p, _p, _p, _p],
     "nvfp4_dequant_swizzled": [_p, _p, _p, _i64, _i64, _int, _p, _p],
     "nvfp4_rotate16_f32": [_p, _i64, _i64, _p, _p],
+    "nvfp4_rotate_matrix_f32": [_p, _i64, _i64, _p, _p, _p],
     "mxfp4_rotquant": [_p, _i64, _i64, _int, _p, _p, _p],
     "mxfp4_rotquant_f32": [_p, _i64, _i64, _int, _p, _p, _p],
     "mxfp4_dequant": [_p, _p, _i64, _i64, _int, _p, _p],
@@ -294,6 +296,21 @@ def rotate16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> t
     _buf(out, rows * cols, torch.float32, x.device, "out")
     fn = _variant(x, "nvfp4_rotate16")
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, _ptr(out), _stream(x.device, stream)))
+    return out
+
+
+def rotate_matrix(x: torch.Tensor, r: torch.Tensor, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """General block rotation: float32 [rows, cols] = x R per 16-element block.
+    r: float32 [16, 16] on x's device, row k multiplying input k."""
+    rows, cols = _check_input(x)
+    _buf(r, 256, torch.float32, x.device, "r")
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.float32, device=x.device)
+    _buf(out, rows * cols, torch.float32, x.device, "out")
+    fn = _variant(x, "nvfp4_rotate_matrix")
+    _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, _ptr(r), _ptr(out),
+                                _stream(x.device, stream)))
     return out
 
 

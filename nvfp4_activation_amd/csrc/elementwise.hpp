@@ -193,5 +193,61 @@ __global__ __launch_bounds__(kThreads) void rotate_kernel(const T* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- general rotation
+
+// Lane s of the quad, broadcast to the whole quad (quad_perm [s, s, s, s]).
+template <int S>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), S * 0x55, 0xF, 0xF, false));
+}
+
+// y = x r for every 16-element block (r: 16 x 16 binary32, row-major, rows
+// are inputs): the Hadamard replaced by a general matrix, as the page "A
+// Fused Hadamard + NVFP4 Quantization Kernel in Triton" proposes in its "Try
+// this" item 3 (a random orthogonal matrix).  Quarter-block layout: each lane
+// gathers its block's 16 inputs from the quad by broadcasts and computes its
+// four outputs y_j = RN(x_0 r_0j), then fused multiply-adds in k order, the
+// summation order the reading fixes.  r is staged in LDS.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rotate_matrix_kernel(const T* __restrict__ x, int64_t nq,
+                                                                 const float* __restrict__ r,
+                                                                 float* __restrict__ y) {
+  __shared__ float4 rs[64];  // row k, columns 4c .. 4c + 3 at rs[4k + c]
+  if (threadIdx.x < 64) rs[threadIdx.x] = reinterpret_cast<const float4*>(r)[threadIdx.x];
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63, t = lane & 3u;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  constexpr int64_t kPerWave = 64 * kQuarters;
+  float4* __restrict__ o = reinterpret_cast<float4*>(y);
+  for (int64_t base = wave * kPerWave; base < nq; base += nwaves * kPerWave) {
+#pragma unroll 2
+    for (int j = 0; j < kQuarters; ++j) {
+      const int64_t pc = base + j * 64 + lane;
+      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (pc < nq) load_quarter(x, pc, z);
+      float xs[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xs[i] = quad_bcast<0>(z[i]);
+        xs[4 + i] = quad_bcast<1>(z[i]);
+        xs[8 + i] = quad_bcast<2>(z[i]);
+        xs[12 + i] = quad_bcast<3>(z[i]);
+      }
+      const float4 r0 = rs[t];
+      float4 acc = make_float4(xs[0] * r0.x, xs[0] * r0.y, xs[0] * r0.z, xs[0] * r0.w);
+#pragma unroll
+      for (int k = 1; k < 16; ++k) {
+        const float4 rk = rs[4 * k + t];
+        acc.x = __builtin_fmaf(xs[k], rk.x, acc.x);
+        acc.y = __builtin_fmaf(xs[k], rk.y, acc.y);
+        acc.z = __builtin_fmaf(xs[k], rk.z, acc.z);
+        acc.w = __builtin_fmaf(xs[k], rk.w, acc.w);
+      }
+      if (pc < nq) o[pc] = acc;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace nvfp4rq

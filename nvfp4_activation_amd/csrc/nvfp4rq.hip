@@ -453,6 +453,27 @@ nvfp4_status rotate_only(const T* x, int64_t rows, int64_t cols, float* y, hipSt
              ? NVFP4_OK
              : NVFP4_ERR_HIP;
 }
+
+template <typename T>
+nvfp4_status rotate_matrix(const T* x, int64_t rows, int64_t cols, const float* r, float* y,
+                           hipStream_t st) {
+  int64_t nb = 0;
+  nvfp4_status s = check_shape(rows, cols, &nb);
+  if (s != NVFP4_OK) return s;
+  const int64_t n = rows * cols;
+  if ((n != 0 && (!x || !y)) || !r) return NVFP4_ERR_NULL;
+  if ((n != 0 && (!aligned(x, 16) || !aligned(y, 16))) || !aligned(r, 16)) return NVFP4_ERR_ALIGN;
+  const Range ry = range_of(y, n * 4);
+  if (overlap(range_of(x, n * static_cast<int64_t>(sizeof(T))), ry) || overlap(range_of(r, 1024), ry))
+    return NVFP4_ERR_ARG;
+  if (nb == 0) return NVFP4_OK;
+  const int64_t nq = 4 * nb;
+  return launch(rotate_matrix_kernel<T>, dim3(quarter_grid(nq)), dim3(kThreads), st, x, nq, r, y) ==
+                 hipSuccess
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
+
 template <typename SMAP>
 nvfp4_status dequant(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t rows,
                      int64_t cols, int rotate, float* y_out, hipStream_t stream, int64_t s_bytes,
@@ -618,6 +639,16 @@ nvfp4_status mxfp4_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int
   const float* no_gscale = nullptr;
   return rotate ? launch_decode<true>(q, s, no_gscale, nq, y_out, Mxfp4Scales{}, stream)
                 : launch_decode<false>(q, s, no_gscale, nq, y_out, Mxfp4Scales{}, stream);
+}
+
+nvfp4_status nvfp4_rotate_matrix(const uint16_t* x_bf16, int64_t rows, int64_t cols, const float* r16,
+                                 float* y_out, hipStream_t stream) {
+  return rotate_matrix(x_bf16, rows, cols, r16, y_out, stream);
+}
+
+nvfp4_status nvfp4_rotate_matrix_f32(const float* x, int64_t rows, int64_t cols, const float* r16,
+                                     float* y_out, hipStream_t stream) {
+  return rotate_matrix(x, rows, cols, r16, y_out, stream);
 }
 
 nvfp4_status nvfp4_stream_calibrate(const uint16_t* x_bf16, int64_t rows, int64_t cols,

@@ -3,9 +3,11 @@
 The study of section 5 of the page "A Fused Hadamard + NVFP4 Quantization
 Kernel in Triton" (does the 16-point rotation lower the relative L2 error
 ||dequant(quant(x)) - x|| / ||x||?), together with its "Try this" item 2 (the
-same question under MXFP4: 32-element blocks, power-of-two scales).  Every
-encode and decode runs in the library's kernels; only the two norms are taken
-with PyTorch, in fp64, on the device.
+same question under MXFP4: 32-element blocks, power-of-two scales) and item 3
+(a random orthogonal 16 x 16 matrix in place of the Hadamard: rotate by R,
+quantize and decode with the built-in rotation off, rotate back by R
+transposed).  Every rotation, encode and decode runs in the library's kernels;
+only the two norms are taken with PyTorch, in fp64, on the device.
 
 Cases: the page's three 256 x 64 tensors, drawn with PyTorch's CPU generator
 from seed 0 in the page's order (normal with columns 3, 17 and 40 scaled by
@@ -61,19 +63,46 @@ def mxfp4_error(x: torch.Tensor, rotate: bool, cols=None) -> float:
     return relative_error(x, nv.mx_dequant(q, s, rotate=rotate), cols)
 
 
+def orthogonal(device, seed: int = 0) -> torch.Tensor:
+    """The random orthogonal matrix (seeded Haar draw from the generators at
+    the repository root), on the device."""
+    _root_on_path()
+    import synth
+    return torch.from_numpy(synth.random_orthogonal16(seed)).to(device)
+
+
+def nvfp4_orth_error(x: torch.Tensor, r: torch.Tensor, cols=None) -> float:
+    q, s, g, _ = nv.rotquant(nv.rotate_matrix(x, r), rotate=False)
+    back = nv.rotate_matrix(nv.dequant(q, s, g, rotate=False), r.t().contiguous())
+    return relative_error(x, back, cols)
+
+
+def mxfp4_orth_error(x: torch.Tensor, r: torch.Tensor, cols=None) -> float:
+    q, s = nv.mx_rotquant(nv.rotate_matrix(x, r), rotate=False)
+    back = nv.rotate_matrix(nv.mx_dequant(q, s, rotate=False), r.t().contiguous())
+    return relative_error(x, back, cols)
+
+
 def study_row(x: torch.Tensor, cols=None) -> dict:
+    r = orthogonal(x.device)
     return {"nvfp4_plain": nvfp4_error(x, False, cols), "nvfp4_rotated": nvfp4_error(x, True, cols),
-            "mxfp4_plain": mxfp4_error(x, False, cols), "mxfp4_rotated": mxfp4_error(x, True, cols)}
+            "nvfp4_orth": nvfp4_orth_error(x, r, cols),
+            "mxfp4_plain": mxfp4_error(x, False, cols), "mxfp4_rotated": mxfp4_error(x, True, cols),
+            "mxfp4_orth": mxfp4_orth_error(x, r, cols)}
 
 
 def page_study(device="cuda:0") -> dict:
     return {name: study_row(t.to(device), cols) for name, (t, cols) in page_tensors().items()}
 
 
-def workload_study(rows_cap: int, device="cuda:0") -> dict:
+def _root_on_path():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     if root not in sys.path:
         sys.path.insert(0, root)
+
+
+def workload_study(rows_cap: int, device="cuda:0") -> dict:
+    _root_on_path()
     import numpy as np
     import synth
     out = {}
@@ -88,11 +117,12 @@ def workload_study(rows_cap: int, device="cuda:0") -> dict:
 
 
 def table(rows: dict) -> str:
-    head = ("| case | NVFP4 plain | NVFP4 rotated | MXFP4 plain | MXFP4 rotated |\n"
-            "|---|---|---|---|---|\n")
+    head = ("| case | NVFP4 plain | NVFP4 Hadamard | NVFP4 random orth. | MXFP4 plain | "
+            "MXFP4 Hadamard | MXFP4 random orth. |\n|---|---|---|---|---|---|---|\n")
     return head + "".join(
-        f"| {k} | {v['nvfp4_plain']:.4f} | {v['nvfp4_rotated']:.4f} | "
-        f"{v['mxfp4_plain']:.4f} | {v['mxfp4_rotated']:.4f} |\n" for k, v in rows.items())
+        f"| {k} | {v['nvfp4_plain']:.4f} | {v['nvfp4_rotated']:.4f} | {v['nvfp4_orth']:.4f} | "
+        f"{v['mxfp4_plain']:.4f} | {v['mxfp4_rotated']:.4f} | {v['mxfp4_orth']:.4f} |\n"
+        for k, v in rows.items())
 
 
 def main() -> int:

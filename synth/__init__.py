@@ -139,6 +139,17 @@ def kv_heads(tokens: int, heads: int, dim: int, seed: int = 0):
 
 # ---------------------------------------------------------------- named workloads
 
+def random_orthogonal16(seed: int = 0) -> np.ndarray:
+    """A random orthogonal 16 x 16 matrix, binary32: Q of the QR factorisation
+    of a seeded standard-normal matrix, each column's sign chosen so that the
+    triangular factor has a positive diagonal (the Haar-distributed draw).
+    The matrix is an input of the general block rotation; numpy's QR is the
+    library routine that draws it."""
+    g = normal_f64(256, seed=seed, stream=11).reshape(16, 16)
+    q, r = np.linalg.qr(g)
+    return (q * np.sign(np.diag(r))).astype(np.float32)
+
+
 @dataclass
 class Workload:
     """One synthetic activation tensor plus the facts its recipe plants."""

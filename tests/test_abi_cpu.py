@@ -38,6 +38,8 @@ def lib():
     lib.mxfp4_dequant.argtypes = [p, p, i64, i64, i, p, p]
     for name in ("nvfp4_rotate16", "nvfp4_rotate16_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, p, p]
+    for name in ("nvfp4_rotate_matrix", "nvfp4_rotate_matrix_f32"):
+        getattr(lib, name).argtypes = [p, i64, i64, p, p, p]
     for name in ("nvfp4_rotquant_swizzled", "nvfp4_rotquant_swizzled_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p]
     lib.nvfp4_dequant_swizzled.argtypes = [p, p, p, i64, i64, i, p, p]
@@ -61,7 +63,7 @@ def test_header_declares_the_boundary():
                  "nvfp4_rotquant_swizzled_f32", "nvfp4_dequant_swizzled",
                  "nvfp4_swizzled_scale_bytes", "nvfp4_rotquant_timed",
                  "nvfp4_rotquant_f32_timed", "nvfp4_stream_calibrate",
-                 "nvfp4_stream_calibrate_f32"):
+                 "nvfp4_stream_calibrate_f32", "nvfp4_rotate_matrix", "nvfp4_rotate_matrix_f32"):
         assert must in names
 
 
@@ -205,6 +207,23 @@ def test_rotate_validation(lib, name):
     assert f(X, 4, 64, Y + 4, None) == ERR_ALIGN
     assert f(X, 4, 64, X + 64, None) == ERR_ARG
     assert f(None, 0, 64, None, None) == OK
+
+
+@pytest.mark.parametrize("name", ["nvfp4_rotate_matrix", "nvfp4_rotate_matrix_f32"])
+def test_rotate_matrix_validation(lib, name):
+    f = getattr(lib, name)
+    Y, R = 0x80000, 0x200000
+    assert f(None, 4, 64, R, Y, None) == ERR_NULL
+    assert f(X, 4, 64, None, Y, None) == ERR_NULL
+    assert f(X, 4, 64, R, None, None) == ERR_NULL
+    assert f(X, 4, 40, R, Y, None) == ERR_SHAPE
+    assert f(X + 8, 4, 64, R, Y, None) == ERR_ALIGN
+    assert f(X, 4, 64, R + 4, Y, None) == ERR_ALIGN
+    assert f(X, 4, 64, R, Y + 4, None) == ERR_ALIGN
+    assert f(X, 4, 64, R, X + 64, None) == ERR_ARG          # output over the input
+    assert f(X, 4, 64, Y + 256, Y, None) == ERR_ARG         # output over the matrix
+    assert f(None, 0, 64, R, None, None) == OK
+    assert f(None, 0, 64, None, None, None) == ERR_NULL
 
 
 def test_swizzled_scale_bytes(lib):

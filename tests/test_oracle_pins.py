@@ -633,14 +633,6 @@ def test_swizzle_worked_positions():
 
 # ---------------------------------------------------------------- general block rotation ("Try this" 3)
 
-def random_orthogonal16(seed: int) -> np.ndarray:
-    """Q of the QR factorisation of a seeded 16 x 16 Gaussian matrix (signs
-    fixed so that R has a positive diagonal), rounded to binary32."""
-    rng = np.random.default_rng(seed)
-    q, r = np.linalg.qr(rng.standard_normal((16, 16)))
-    return (q * np.sign(np.diag(r))).astype(np.float32)
-
-
 def test_rotate_matrix_identity_and_permutation():
     rng = np.random.default_rng(31)
     x = (rng.standard_normal((5, 64)) * 1e3).astype(np.float32)
@@ -668,7 +660,7 @@ def test_rotate_matrix_follows_the_fused_multiply_add_order():
     bit for bit on random blocks and a random orthogonal matrix (a separately
     rounded multiply and add, or another order, differs on such data)."""
     rng = np.random.default_rng(33)
-    R = random_orthogonal16(5)
+    R = synth.random_orthogonal16(5)
     x = (rng.standard_normal((3, 16 * 8)) * np.exp2(rng.uniform(-20, 20, size=(3, 1)))).astype(np.float32)
     got = oracle.rotate_matrix(x, R).reshape(-1, 16)
     Rf = [[em.f32_to_frac(R[k, j]) for j in range(16)] for k in range(16)]
@@ -696,7 +688,7 @@ def test_rotate_matrix_error_bound_and_round_trip():
     rotating back with R^T returns x up to the same kind of bound (plus R's
     own distance from orthogonality)."""
     rng = np.random.default_rng(34)
-    R = random_orthogonal16(6)
+    R = synth.random_orthogonal16(6)
     x = (rng.standard_normal((40, 160)) * 3.0).astype(np.float32)
     xb = x.reshape(-1, 16).astype(np.float64)
     R64 = R.astype(np.float64)

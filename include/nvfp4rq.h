@@ -34,8 +34,10 @@
  *   - Pointers marked "device" must be device memory of the current HIP
  *     device (or memory it can access).  The caller owns every buffer; the
  *     library allocates nothing and keeps no state between calls.
- *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
- *     without waiting for it.  Nothing is read back to the host.
+ *   - Work is enqueued on `stream` (0 = the null stream), which must belong
+ *     to the current HIP device (launch shapes are sized for that device),
+ *     and the call returns without waiting for it.  Nothing is read back to
+ *     the host.
  *   - Validation happens before anything is enqueued: a non-zero status means
  *     no work was enqueued and no output was touched.  NVFP4_ERR_HIP means a
  *     launch was rejected by the runtime; earlier launches of the same call

@@ -14,6 +14,7 @@ Hadamard rotation).
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -98,6 +99,20 @@ def _stream(device: torch.device, stream=None) -> int:
     return stream.cuda_stream
 
 
+def _on_device(fn):
+    """Run the call with its first tensor's GPU as the current device, so that
+    the library sizes its launches for that device and launches there (the
+    stream passed down belongs to the same device).  Host tensors go through
+    unchanged, to be refused by the call's own checks."""
+    @functools.wraps(fn)
+    def call(t, *args, **kwargs):
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            with torch.cuda.device(t.device):
+                return fn(t, *args, **kwargs)
+        return fn(t, *args, **kwargs)
+    return call
+
+
 def _variant(x: torch.Tensor, base: str) -> str:
     if x.dtype == torch.bfloat16:
         return base
@@ -150,6 +165,7 @@ def _decode_inputs(q, s, g, s_numel):
         _buf(g, 1, torch.float32, q.device, "g")
 
 
+@_on_device
 def rotamax(x: torch.Tensor, rotate: bool = True, amax: torch.Tensor | None = None,
             stream=None) -> torch.Tensor:
     """Pass 1: the rotated global amax, as a float32 device tensor [1]."""
@@ -163,6 +179,7 @@ def rotamax(x: torch.Tensor, rotate: bool = True, amax: torch.Tensor | None = No
     return amax
 
 
+@_on_device
 def quant_from_amax(x: torch.Tensor, amax: torch.Tensor, rotate: bool = True,
                     out: tuple | None = None, stream=None):
     """Pass 2: global scale from a device amax, then rotate+quantize.
@@ -184,6 +201,7 @@ def quant_from_amax(x: torch.Tensor, amax: torch.Tensor, rotate: bool = True,
     return q, s, g
 
 
+@_on_device
 def rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, stream=None):
     """Both passes.  x: bfloat16 or float32 [rows, cols], cols % 16 == 0.
     Returns (q uint8 [rows, cols/2], s uint8 [rows, cols/16] E4M3FN bytes,
@@ -203,6 +221,7 @@ def rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, str
     return q, s, g, a
 
 
+@_on_device
 def rotquant_timed(x: torch.Tensor, events: list, rotate: bool = True, out: tuple | None = None,
                    stream=None):
     """rotquant with each launched kernel timed in place: events is a list of
@@ -229,6 +248,7 @@ def rotquant_timed(x: torch.Tensor, events: list, rotate: bool = True, out: tupl
     return q, s, g, a, nk.value
 
 
+@_on_device
 def dequant(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = True,
             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Decode codes and scales back to float32 [rows, cols] (inverse rotation
@@ -255,6 +275,7 @@ def swizzled_scale_bytes(rows: int, cols: int) -> int:
     return n
 
 
+@_on_device
 def rotquant_swizzled(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, stream=None):
     """rotquant with the block scales in the 128 x 4-tile swizzled layout.
     Returns (q uint8 [rows, cols/2], s uint8 [swizzled_scale_bytes], g, amax)."""
@@ -273,6 +294,7 @@ def rotquant_swizzled(x: torch.Tensor, rotate: bool = True, out: tuple | None = 
     return q, s, g, a
 
 
+@_on_device
 def dequant_swizzled(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: bool = True,
                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     if q.dim() != 2:
@@ -288,6 +310,7 @@ def dequant_swizzled(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor, rotate: 
     return out
 
 
+@_on_device
 def rotate16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """The block rotation alone: float32 [rows, cols] = x H16 per 16-element block."""
     rows, cols = _check_input(x)
@@ -299,6 +322,7 @@ def rotate16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> t
     return out
 
 
+@_on_device
 def rotate_matrix(x: torch.Tensor, r: torch.Tensor, out: torch.Tensor | None = None,
                   stream=None) -> torch.Tensor:
     """General block rotation: float32 [rows, cols] = x R per 16-element block.
@@ -314,6 +338,7 @@ def rotate_matrix(x: torch.Tensor, r: torch.Tensor, out: torch.Tensor | None = N
     return out
 
 
+@_on_device
 def mx_rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, stream=None):
     """MXFP4 single pass.  x: bfloat16 or float32 [rows, cols], cols % 32 == 0.
     Returns (q uint8 [rows, cols/2], s uint8 [rows, cols/32] E8M0 bytes)."""
@@ -331,6 +356,7 @@ def mx_rotquant(x: torch.Tensor, rotate: bool = True, out: tuple | None = None, 
     return q, s
 
 
+@_on_device
 def mx_dequant(q: torch.Tensor, s: torch.Tensor, rotate: bool = True,
                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     if s.dim() != 2 or q.dim() != 2:
@@ -347,6 +373,7 @@ def mx_dequant(q: torch.Tensor, s: torch.Tensor, rotate: bool = True,
     return out
 
 
+@_on_device
 def stream_calibrate(x: torch.Tensor, out: tuple | None = None, stream=None):
     """Measurement support: the fused call's launch sequence with no-arithmetic
     twins of its two kernels (same grids, access patterns and bytes).  Returns

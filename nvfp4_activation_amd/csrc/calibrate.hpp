@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_bf16_kernel(const uint16
                                                                     uint32_t* __restrict__ out,
                                                                     int partials, int64_t nt_end) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t wave = pass1_wg() * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
   const int64_t npieces = 2 * nb;
   constexpr int64_t kPerWave = 64 * kAmaxPieces;

@@ -12,7 +12,10 @@ namespace nvfp4rq {
 namespace {  // one translation unit (nvfp4rq.hip): internal linkage
 
 constexpr int kThreads = 256;      // 4 waves of 64
-constexpr int kAmaxPieces = 8;     // 16-byte pieces per lane per iteration in the bf16 amax pass
+// 16-byte pieces per lane per iteration in the bf16 amax pass: 4 KiB per
+// wave.  Against 8: pass 1 at 16384 x 8192 42.0 instead of 44.9 us, at
+// 32768 x 14336 132 instead of 141 us; 2 and 16 were slower than both.
+constexpr int kAmaxPieces = 4;
 
 // The fast path (corrected divisions with per-scale reciprocals) is used for
 // bf16 input when the global amax lies in [2^-38, 2^15): then every divisor is
@@ -46,6 +49,23 @@ __host__ __device__ constexpr int64_t head_bytes(int64_t npartials) {
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Logical workgroup index of the bf16 amax pass.  Workgroups go round-robin
+// to the 8 XCDs (XCD b % 8), and a logical workgroup iteration reads
+// kAmaxPieces / 2 = 2 chunks of 256 blocks.  Physical workgroup b, the j-th on
+// its XCD (j = b / 8), becomes 16 (j / 2) + 2 (b % 8) + j % 2, so each XCD
+// reads runs of 4 consecutive chunks: chunk c on XCD (c / 4) % 8, the XCD on
+// which the quantize pass's order visits it (RowMajorScales::order), which
+// then finds it in that XCD's L2 (16384 x 8192 step: 98.6 -> 97.5 us;
+// 4096 x 4096: 21.4 -> 20.2 us).  A bijection when the grid is a multiple of
+// 16; other grids keep b.
+static_assert(kAmaxPieces == 4, "pass1_wg pairs workgroups of two chunks each");
+__device__ __forceinline__ int64_t pass1_wg() {
+  const int64_t b = blockIdx.x;
+  if (gridDim.x % 16 != 0) return b;
+  const int64_t j = b >> 3;
+  return 16 * (j >> 1) + 2 * (b & 7) + (j & 1);
+}
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
 #pragma unroll

@@ -29,18 +29,21 @@ namespace {  // one translation unit (nvfp4rq.hip): internal linkage
 struct RowMajorScales {
   static constexpr int kSub = 1;
   static constexpr bool kStaged = false;
-  int xcd_order;  // visit chunks on the XCD that read them in pass 1
+  int xcd_order;  // give each XCD runs of 4 consecutive chunks
   int mirror;     // a workgroup per chunk, workgroup i taking chunk nchunks - 1 - i
   __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
   __host__ __device__ int64_t chunks(int64_t nb) const { return (nb + kThreads - 1) / kThreads; }
-  // Workgroups go round-robin to the 8 XCDs, each with its own L2, and the L2
-  // keeps what pass 1 read last across the kernel boundary.  bf16 chunk c
-  // (8 KiB of input) was read by wave c % 4 of pass-1 workgroup c / 4, on XCD
-  // (c / 4) % 8 (both grids are multiples of 8); visit index i runs on XCD
-  // i % 8, so within each group of 32 chunks index i takes the chunk read on
-  // its own XCD.  At 16384 x 8192 this takes 5 us off the pass on a box whose
-  // last-level cache gave it nothing.  Set only when the chunk count is a
-  // multiple of 32, so the order is a permutation of the chunks.
+  // Workgroups go round-robin to the 8 XCDs, each with its own L2 and address
+  // translation caches.  The order gives each XCD runs of 4 consecutive
+  // chunks (32 KiB of bf16 input): visit index i runs on XCD i % 8 and takes
+  // chunk (i & ~31) | ((i & 7) << 2) | ((i >> 3) & 3), a permutation within
+  // each group of 32 chunks.  The bf16 amax pass reads chunk c on XCD
+  // (c / 4) % 8 too (pass1_wg), so the chunks it read last are still in the
+  // visiting XCD's L2.  The run length pays by itself as well: before the
+  // amax pass matched it, pass 2 at 16384 x 8192 took 56.2, 55.2, 53.3 and
+  // 53.3 us with runs of 1, 2, 4 and 8 chunks on one box, and 53.5, 54.0,
+  // 54.0, 54.9 and 57.2 us with runs of 4, 8, 16, 64 and 256 on another.
+  // Set only when the chunk count is a multiple of 32.
   // With a workgroup per chunk the dispatcher starts workgroups in index
   // order, so mirror keeps the last chunks (the likeliest to be still cached
   // after an amax pass) first.

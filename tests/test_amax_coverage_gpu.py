@@ -1,0 +1,61 @@
+"""Every chunk of the input reaches the global amax, whatever the amax pass's
+grid: a zero tensor with one planted value, moved through every 256-block
+chunk (and through the lane and piece positions inside the chunks), must give
+the planted value's rotated magnitude each time.  The amax pass maps its
+workgroups to the input through an XCD-pairing remap when its grid is a
+multiple of 16 and directly otherwise; a mapping that skipped or repeated a
+region would lose the planted value there."""
+from __future__ import annotations
+
+import sys
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def nv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_activation_amd as nv
+    return nv
+
+
+@pytest.mark.parametrize("amax_wgs", [None, 48, 24])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
+    if amax_wgs is None:
+        monkeypatch.delenv("NVFP4RQ_AMAX_WGS", raising=False)
+    else:
+        monkeypatch.setenv("NVFP4RQ_AMAX_WGS", str(amax_wgs))
+    rows = cols = 4096
+    nchunks = rows * cols // 16 // 256
+    say(f"amax coverage: {nchunks} chunks, amax_wgs={amax_wgs}, rotate={rotate}")
+    dev = "cuda:0"
+    x = torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev)
+    flat = x.view(-1)
+    out = (torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
+           torch.empty(rows, cols // 16, dtype=torch.uint8, device=dev),
+           torch.empty(1, dtype=torch.float32, device=dev),
+           torch.empty(1, dtype=torch.float32, device=dev))
+    got = torch.empty(nchunks, dtype=torch.float32, device=dev)
+    big = 1024.0                       # exact in bf16; rotated, every output is +-256
+    # element planted in chunk c: block (c * 37) % 256 of the chunk, lane c % 16
+    pos = torch.tensor([(c * 256 + (c * 37) % 256) * 16 + c % 16 for c in range(nchunks)],
+                       dtype=torch.int64, device=dev)
+    # device-side index views and copies only: the loop never waits for the GPU
+    for c in range(nchunks):
+        flat.index_fill_(0, pos[c:c + 1], big)
+        nv.rotquant(x, rotate=rotate, out=out)
+        got[c:c + 1].copy_(out[3])
+        flat.index_fill_(0, pos[c:c + 1], 0.0)
+    torch.cuda.synchronize()
+    want = big / 4 if rotate else big
+    missed = (got != want).nonzero().flatten().tolist()
+    assert not missed, f"chunks whose planted value was lost: {missed[:20]} ({len(missed)} in all)"

@@ -374,7 +374,9 @@ nvfp4_status rotquant_swizzled(const T* x, int64_t rows, int64_t cols, int rotat
   nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, false, sbytes);
   if (r != NVFP4_OK) return r;
   const uint32_t cb = static_cast<uint32_t>(cols / 16), ctiles = (cb + 3) / 4;
-  return enqueue_both(x, nb, rotate, q, s, g, amax, st, SwizzledScales{rows, cb, ctiles, (cb + 15) / 16});
+  SwizzledScales sm{rows, cb, ctiles, (cb + 15) / 16};
+  sm.runs16 = sm.cs % 16 == 0 && sm.chunks(nb) % 128 == 0 ? 1 : 0;
+  return enqueue_both(x, nb, rotate, q, s, g, amax, st, sm);
 }
 
 template <typename T>

@@ -390,7 +390,8 @@ def test_dequant_small_shapes(nv, rows, cols, rotate):
 
 # ---------------------------------------------------------------- swizzled scales
 
-SWZ_SHAPES = [(1, 16), (3, 48), (127, 16), (128, 64), (129, 80), (300, 4112), (257, 8192)]
+SWZ_SHAPES = [(1, 16), (3, 48), (127, 16), (128, 64), (129, 80), (300, 4112), (257, 8192),
+              (1000, 4096), (2000, 8192)]   # the last two: 16-chunk runs per XCD, ragged last tile
 
 
 @pytest.mark.parametrize("rows,cols", SWZ_SHAPES)

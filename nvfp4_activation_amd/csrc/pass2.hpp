@@ -204,6 +204,32 @@ __device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, 
     f->load(x, b);
 }
 
+// The lane's block of the workgroup's second chunk (bf16, row-major), loaded
+// before the prologue straight into LDS (the kernel has no registers to spare
+// for it), 8 KiB per workgroup: 16384 x 8192 step 97.5 -> 95.7 us, pass 2
+// 52.6 -> 51.1 us (three A/B pairs).  Used from 3 chunks per workgroup: with
+// 2 (4096 x 4096) the prologue, whose wait for the maxima also waits for
+// these loads, made the step 0.25 us slower.  quant_blocks_rm reads the
+// block back under the same condition.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+__device__ __forceinline__ bool prefetches_second(int64_t mine) { return mine >= 3; }
+__device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, int64_t nb,
+                                                RowMajorScales smap, uint4 (*pre)[kThreads]) {
+  const int64_t nchunks = smap.chunks(nb);
+  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  if (!prefetches_second(mine)) return;
+  const int64_t b = smap.order((mine - 2) * gridDim.x + blockIdx.x, nchunks) * kThreads + threadIdx.x;
+  if (b >= nb) return;
+  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
+  // The destination operand is per wave: lane l's 16 bytes land at slot
+  // 64 w + l, i.e. at pre[.][threadIdx.x].  Address-space conversions take
+  // C-style casts.
+  const int w = threadIdx.x >> 6;
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(p), (lds_void_ptr)(&pre[0][w * 64]), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(&pre[1][w * 64]), 16, 0, 0);
+}
+
 // One block of pass 2, in one lane: rotation (in place on lo, hi), the block
 // scale byte and the two words of E2M1 codes.  Every step is the definition
 // of section 2 (hadamard_nvfp4_kernel) in binary32:
@@ -281,12 +307,13 @@ __device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, 
 // chunk first: the chunks pass 1 read last are the likeliest to still be in
 // the last-level cache.  The first chunk's blocks were loaded before the
 // prologue, so its iteration is peeled off.
-template <typename T, bool ROTATE, bool FAST>
+template <typename T, bool ROTATE, bool FAST, bool PRE>
 __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t nb, float g,
                                                 const float2* __restrict__ tab,
                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                                 RowMajorScales smap, const HeadGuard& head,
-                                                const FirstBlock<T>& first) {
+                                                const FirstBlock<T>& first,
+                                                const uint4 (*pre)[kThreads]) {
   const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
@@ -311,7 +338,19 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
       finish(chunk, lo, hi);
     }
   }
-  for (int64_t it = mine - 2; it >= 0; --it) {
+  int64_t it = mine - 2;
+  if (PRE && prefetches_second(mine)) {  // the second chunk, from LDS (see prefetch_second)
+    const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
+    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
+    if (chunk * kThreads + threadIdx.x < nb) {
+      float lo[8], hi[8];
+      widen8(pre[0][threadIdx.x], lo);
+      widen8(pre[1][threadIdx.x], hi);
+      finish(chunk, lo, hi);
+    }
+    --it;
+  }
+  for (; it >= 0; --it) {
     const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
     if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
     if (chunk * kThreads + threadIdx.x < nb) {
@@ -375,6 +414,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   __shared__ uint32_t red[kThreads / 64];
   FirstBlock<T> first;
   if constexpr (!SMAP::kStaged) load_first(x, nb, smap, &first);  // staged: no registers to spare
+  constexpr bool kPre = !SMAP::kStaged && sizeof(T) == 2;
+  __shared__ uint4 pre[kPre ? 2 : 1][kThreads];
+  if constexpr (kPre) prefetch_second(x, nb, smap, pre);
   HeadGuard head{nullptr, 0, 0, spin_limit, gscale_out};
   uint32_t abits;
   if (npartials == 0) {
@@ -412,14 +454,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       if constexpr (SMAP::kStaged)
         quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head);
       else
-        quant_blocks_rm<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head, first);
+        quant_blocks_rm<T, ROTATE, true, kPre>(x, nb, g, tab, q, s, smap, head, first, pre);
       return;
     }
   }
   if constexpr (SMAP::kStaged)
     quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head);
   else
-    quant_blocks_rm<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head, first);
+    quant_blocks_rm<T, ROTATE, false, kPre>(x, nb, g, tab, q, s, smap, head, first, pre);
 }
 
 }  // namespace

@@ -215,19 +215,21 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
 __device__ __forceinline__ bool prefetches_second(int64_t mine) { return mine >= 3; }
 __device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, int64_t nb,
-                                                RowMajorScales smap, uint4 (*pre)[kThreads]) {
+                                                RowMajorScales smap, uint4* pre) {
   const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   if (!prefetches_second(mine)) return;
   const int64_t b = smap.order((mine - 2) * gridDim.x + blockIdx.x, nchunks) * kThreads + threadIdx.x;
   if (b >= nb) return;
   const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
-  // The destination operand is per wave: lane l's 16 bytes land at slot
-  // 64 w + l, i.e. at pre[.][threadIdx.x].  Address-space conversions take
-  // C-style casts.
+  // pre holds the blocks' first halves at [0, kThreads) and their second
+  // halves at [kThreads, 2 kThreads).  The destination operand is per wave:
+  // lane l's 16 bytes land at slot 64 w + l, i.e. at threadIdx.x.
+  // Address-space conversions take C-style casts.
   const int w = threadIdx.x >> 6;
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(p), (lds_void_ptr)(&pre[0][w * 64]), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(&pre[1][w * 64]), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(p), (lds_void_ptr)(pre + w * 64), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(pre + kThreads + w * 64), 16, 0,
+                                   0);
 }
 
 // One block of pass 2, in one lane: rotation (in place on lo, hi), the block
@@ -313,7 +315,7 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                                 RowMajorScales smap, const HeadGuard& head,
                                                 const FirstBlock<T>& first,
-                                                const uint4 (*pre)[kThreads]) {
+                                                const uint4* pre) {
   const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
@@ -344,8 +346,8 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
     if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
     if (chunk * kThreads + threadIdx.x < nb) {
       float lo[8], hi[8];
-      widen8(pre[0][threadIdx.x], lo);
-      widen8(pre[1][threadIdx.x], hi);
+      widen8(pre[threadIdx.x], lo);
+      widen8(pre[kThreads + threadIdx.x], hi);
       finish(chunk, lo, hi);
     }
     --it;
@@ -415,8 +417,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   FirstBlock<T> first;
   if constexpr (!SMAP::kStaged) load_first(x, nb, smap, &first);  // staged: no registers to spare
   constexpr bool kPre = !SMAP::kStaged && sizeof(T) == 2;
-  __shared__ uint4 pre[kPre ? 2 : 1][kThreads];
-  if constexpr (kPre) prefetch_second(x, nb, smap, pre);
+  __shared__ uint4 pre[kPre ? 2 : 1][kPre ? kThreads : 1];  // one element where unused
+  if constexpr (kPre) prefetch_second(x, nb, smap, &pre[0][0]);
   HeadGuard head{nullptr, 0, 0, spin_limit, gscale_out};
   uint32_t abits;
   if (npartials == 0) {
@@ -454,14 +456,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       if constexpr (SMAP::kStaged)
         quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head);
       else
-        quant_blocks_rm<T, ROTATE, true, kPre>(x, nb, g, tab, q, s, smap, head, first, pre);
+        quant_blocks_rm<T, ROTATE, true, kPre>(x, nb, g, tab, q, s, smap, head, first, &pre[0][0]);
       return;
     }
   }
   if constexpr (SMAP::kStaged)
     quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head);
   else
-    quant_blocks_rm<T, ROTATE, false, kPre>(x, nb, g, tab, q, s, smap, head, first, pre);
+    quant_blocks_rm<T, ROTATE, false, kPre>(x, nb, g, tab, q, s, smap, head, first, &pre[0][0]);
 }
 
 }  // namespace

@@ -137,12 +137,25 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
   if (threadIdx.x < 64) {  // wave 0: one counter per lane
     uint32_t spins = 0;
     int late = 0;
-    // Relaxed: acquire/release at agent scope would write back or invalidate
-    // the L2 of every XCD involved on each poll.  Nothing written by other
-    // workgroups is read after the wait; the waiter's stores follow the loop.
+    // Each poll reads a counter with a fetch-and-add of zero: an atomic,
+    // performed where the increments are performed.  A relaxed agent-scope
+    // load (global_load sc1) may instead be answered by the XCD's own L2,
+    // which can still hold the line as the amax pass's clearing store left it
+    // on XCD 0, where most waiters run; once streaming traffic stops evicting
+    // that line, such a waiter saw a stale sum until its spin limit ran out
+    // (a few calls in 10^4 at 4096 x 4096 with a 48-workgroup amax pass).
+    // Relaxed ordering: acquire/release at agent scope would write back or
+    // invalidate the L2 of every XCD involved on each poll.  Nothing written
+    // by other workgroups is read after the wait; the waiter's stores follow
+    // the loop.
+    // The compiler turns an add of a literal 0 back into a load, so the zero
+    // is made opaque to it (an empty asm statement that only claims to
+    // change the register).
+    uint32_t zero = 0u;
+    __asm__ volatile("" : "+v"(zero));
     for (;;) {
-      uint32_t c = __hip_atomic_load(h.counters + threadIdx.x * kCounterStride, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t c = __hip_atomic_fetch_add(h.counters + threadIdx.x * kCounterStride, zero, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
       if (c >= h.need) break;

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import sys
 
+import numpy as np
 import pytest
 import torch
 
@@ -45,6 +46,7 @@ def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
            torch.empty(1, dtype=torch.float32, device=dev),
            torch.empty(1, dtype=torch.float32, device=dev))
     got = torch.empty(nchunks, dtype=torch.float32, device=dev)
+    got_g = torch.empty(nchunks, dtype=torch.float32, device=dev)
     big = 1024.0                       # exact in bf16; rotated, every output is +-256
     # element planted in chunk c: block (c * 37) % 256 of the chunk, lane c % 16
     pos = torch.tensor([(c * 256 + (c * 37) % 256) * 16 + c % 16 for c in range(nchunks)],
@@ -54,8 +56,14 @@ def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
         flat.index_fill_(0, pos[c:c + 1], big)
         nv.rotquant(x, rotate=rotate, out=out)
         got[c:c + 1].copy_(out[3])
+        got_g[c:c + 1].copy_(out[2])
         flat.index_fill_(0, pos[c:c + 1], 0.0)
     torch.cuda.synchronize()
     want = big / 4 if rotate else big
     missed = (got != want).nonzero().flatten().tolist()
     assert not missed, f"chunks whose planted value was lost: {missed[:20]} ({len(missed)} in all)"
+    # the global scale of every call (a NaN would mean the quantize pass gave up
+    # waiting for its own workgroups)
+    g = np.float32(np.float32(want) / np.float32(6.0)) / np.float32(448.0)
+    bad_g = (got_g != float(g)).nonzero().flatten().tolist()
+    assert not bad_g, f"calls with a wrong global scale: {bad_g[:20]} ({len(bad_g)} in all)"

@@ -1,5 +1,5 @@
 """Every chunk of the input reaches the global amax, whatever the amax pass's
-grid: a zero tensor with one planted value, moved through every 256-block
+grid, and repeated fused calls never lose their global scale: a zero tensor with one planted value, moved through every 256-block
 chunk (and through the lane and piece positions inside the chunks), must give
 the planted value's rotated magnitude each time.  The amax pass maps its
 workgroups to the input through an XCD-pairing remap when its grid is a
@@ -67,3 +67,33 @@ def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
     g = np.float32(np.float32(want) / np.float32(6.0)) / np.float32(448.0)
     bad_g = (got_g != float(g)).nonzero().flatten().tolist()
     assert not bad_g, f"calls with a wrong global scale: {bad_g[:20]} ({len(bad_g)} in all)"
+
+
+@pytest.mark.parametrize("rows,cols,calls", [(16384, 8192, 400), (2048, 8192, 2000), (4096, 4096, 2000)])
+def test_repeated_calls_keep_the_global_scale(nv, monkeypatch, rows, cols, calls):
+    """Back-to-back fused calls on one set of buffers: every call's amax and
+    global scale equal the oracle's.  A quantize workgroup that writes over the
+    head of q_out first waits for every workgroup to have read pass 1's maxima
+    there; a wait that ran out would leave a NaN global scale."""
+    monkeypatch.delenv("NVFP4RQ_AMAX_WGS", raising=False)
+    monkeypatch.delenv("NVFP4RQ_QUANT_WGS", raising=False)
+    import oracle
+    import synth
+    say(f"repeated calls: {rows}x{cols}, {calls} calls")
+    x = synth.normal_bf16(rows * cols, seed=rows + cols, stream=3).reshape(rows, cols)
+    oq, os_, og, oa = oracle.quantize(x, True)
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    out = (torch.empty(rows, cols // 2, dtype=torch.uint8, device="cuda:0"),
+           torch.empty(rows, cols // 16, dtype=torch.uint8, device="cuda:0"),
+           torch.empty(1, dtype=torch.float32, device="cuda:0"),
+           torch.empty(1, dtype=torch.float32, device="cuda:0"))
+    gs = torch.empty(calls, dtype=torch.float32, device="cuda:0")
+    am = torch.empty(calls, dtype=torch.float32, device="cuda:0")
+    for c in range(calls):
+        nv.rotquant(xd, rotate=True, out=out)
+        gs[c:c + 1].copy_(out[2])
+        am[c:c + 1].copy_(out[3])
+    torch.cuda.synchronize()
+    bad = ((gs != float(np.float32(og))) | (am != float(np.float32(oa)))).nonzero().flatten().tolist()
+    assert not bad, f"calls with a wrong amax or global scale: {bad[:20]} ({len(bad)} in all)"
+    assert np.array_equal(out[0].cpu().numpy(), oq) and np.array_equal(out[1].cpu().numpy(), os_)

@@ -28,7 +28,7 @@ constexpr uint32_t kFastAmaxHi = 0x47000000u;   // 2^15
 // (possible only when the global scale comes from another tensor's amax) take
 // true divisions.
 constexpr float kQuotientLimit = 0x1p100f;
-constexpr int64_t kLastLevelKeep = 144LL << 20;  // bytes of input pass 1 leaves cached
+constexpr int64_t kLastLevelKeep = 160LL << 20;  // bytes of input pass 1 leaves cached
 // From this input size on, the two passes of a row-major call hand the amax
 // over through a zeroed word instead of per-workgroup maxima, so that pass 2
 // can run a workgroup per chunk (see enqueue_both).

@@ -219,9 +219,9 @@ hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* b
   // read last in the 256 MB last-level cache; the part before the last
   // kLastLevelKeep bytes would be evicted before the quantize pass got to it,
   // so pass 1 streams it with non-temporal loads.  Measured at 16384 x 8192
-  // (step, keeping 96 / 128 / 144 / 176 / 240 MB): 103.5 / 101.0 / 100.9 /
-  // 101.0 / 102.5 us; streaming less leaves pass 1 slower, streaming more
-  // costs pass 2 its cache hits.  At 32768 x 14336 the rule takes 12 us off.
+  // (step, keeping 128 / 144 / 160 / 176 MB, two runs each): 96.9 / 96.2 /
+  // 95.9 / 96.1 us; streaming less leaves pass 1 slower, streaming more
+  // costs pass 2 its cache hits.  At 32768 x 14336 the rule took 12 us off.
   const int64_t nt_end = bf16_nt_end(nb);
   return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials, nt_end)
                 : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials,

@@ -83,8 +83,8 @@ typedef enum nvfp4_status {
  *               row-major [rows, cols/2], element 2k in the low nibble of
  *               byte k.  May be NULL when rows * cols == 0.  The call first
  *               keeps pass 1's per-workgroup maxima and arrival counters in
- *               its first bytes (at least about 8 KiB, for tensors of about
- *               1040 blocks or more), so its contents are defined only once
+ *               its first 4 KiB (for tensors of 512 blocks or more), so its
+ *               contents are defined only once
  *               the call has completed on the stream.
  *   s_out       device, rows * cols / 16 bytes, 4-byte aligned: E4M3FN block
  *               scales (0x00..0x7E), row-major [rows, cols/16].  May be NULL

@@ -33,18 +33,19 @@ constexpr int64_t kLastLevelKeep = 160LL << 20;  // bytes of input pass 1 leaves
 // over through a zeroed word instead of per-workgroup maxima, so that pass 2
 // can run a workgroup per chunk (see enqueue_both).
 constexpr int64_t kOneShotInputBytes = 512LL << 20;
-// Arrival counters of the quantize pass when pass 1 leaves its partial maxima
-// in q_out: spread over kCounters words on separate 128-byte lines, since
-// thousands of increments of one word serialize (and a workgroup's loads
-// wait behind its own pending atomic).
-constexpr int kCounters = 64;
-constexpr int kCounterStride = 32;  // words
-__host__ __device__ constexpr int64_t counter_base(int64_t npartials) {
-  return (npartials + kCounterStride - 1) / kCounterStride * kCounterStride;  // words
-}
-__host__ __device__ constexpr int64_t head_bytes(int64_t npartials) {
-  return 4 * (counter_base(npartials) + kCounters * kCounterStride);
-}
+// When pass 1 leaves its per-workgroup maxima in q_out, the head of q_out
+// (the quantize pass's chunks 0 and 1, 2 KiB of codes each) holds the maxima
+// at words [0, npartials), npartials <= kMaxPartials, and the quantize pass's
+// arrival counters in chunk 1, kCounters words on separate 128-byte lines
+// (thousands of increments of one word serialize, and a workgroup's loads
+// wait behind its own pending atomic).  Only the quantize workgroup that
+// writes chunk 0 reads the counters, and it writes chunk 1 as well, after
+// chunk 0: nothing overwrites a counter that is still being read.
+constexpr int kMaxPartials = 512;
+constexpr int kCounters = 16;
+constexpr int kCounterStride = 32;                                               // words
+constexpr int64_t kCounterBase = kMaxPartials;                                   // words
+constexpr int64_t kHeadBytes = 4 * (kCounterBase + kCounters * kCounterStride);  // 4096
 
 // ---------------------------------------------------------------- reductions
 
@@ -96,7 +97,7 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restric
       atomicMax(out, r);
   }
   if (partials && blockIdx.x == 0 && threadIdx.x < kCounters)
-    out[counter_base(gridDim.x) + threadIdx.x * kCounterStride] = 0u;
+    out[kCounterBase + threadIdx.x * kCounterStride] = 0u;
 }
 
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }

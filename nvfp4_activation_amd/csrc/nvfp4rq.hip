@@ -277,13 +277,15 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const uint32_t* a
 }
 
 bool zeroed_word_path(int g1, int64_t nb, bool large) {
-  return head_bytes(g1) > 8 * nb || large || env_int("NVFP4RQ_ZEROED_AMAX");
+  return g1 > kMaxPartials || kHeadBytes > 8 * nb || large || env_int("NVFP4RQ_ZEROED_AMAX");
 }
 
-// Both passes.  When q_out has room (8 nb bytes against head_bytes: from
-// about 1040 blocks up), pass 1 leaves per-workgroup maxima and cleared counters at
-// the head of q_out (which pass 2 overwrites last), so no word has to be
-// zeroed first; smaller tensors take the zeroed-word path.  So do row-major
+// Both passes.  When q_out has room (8 nb bytes against kHeadBytes: from 512
+// blocks up) and pass 1 has at most kMaxPartials workgroups, pass 1 leaves
+// per-workgroup maxima and cleared counters at the head of q_out (which one
+// pass-2 workgroup overwrites last), so no word has to be zeroed first;
+// smaller tensors, wider pass-1 grids and the swizzled layout take the
+// zeroed-word path.  So do row-major
 // inputs of kOneShotInputBytes and more: with the amax in one word, pass 2
 // runs a workgroup per chunk, which streams inputs well past the last-level
 // cache faster than the persistent grid that the per-workgroup maxima call
@@ -298,7 +300,8 @@ nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_
   // per step at 939 MB)
   const bool large = std::is_same_v<SMAP, RowMajorScales> &&
                      nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
-  if (nb == 0 || zeroed_word_path(g1, nb, large)) {
+  // The swizzled layout always takes the amax as one word (see quant_blocks).
+  if (nb == 0 || !std::is_same_v<SMAP, RowMajorScales> || zeroed_word_path(g1, nb, large)) {
     nvfp4_status r = enqueue_rotamax(x, nb, rotate, amax, st);
     if (r != NVFP4_OK) return r;
     return enqueue_quant(x, nb, rotate, reinterpret_cast<const uint32_t*>(amax), 0, amax, q, s, g, st,

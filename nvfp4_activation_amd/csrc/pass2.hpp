@@ -51,7 +51,6 @@ struct RowMajorScales {
     if (mirror) return nchunks - 1 - i;
     return xcd_order ? (i & ~int64_t{31}) | ((i & 7) << 2) | ((i >> 3) & 3) : i;
   }
-  __device__ __forceinline__ int64_t first_q_byte(int64_t chunk) const { return chunk * kThreads * 8; }
   __device__ __forceinline__ bool locate(int64_t chunk, int, uint32_t tid, int64_t nb, int64_t* b,
                                          int64_t* si) const {
     *b = chunk * kThreads + tid;
@@ -75,9 +74,6 @@ struct SwizzledScales {
   __device__ __forceinline__ Tile split(int64_t chunk) const {
     const int64_t rt = chunk / cs;
     return Tile{rt, static_cast<uint32_t>(chunk - rt * cs)};
-  }
-  __device__ __forceinline__ int64_t first_q_byte(Tile t) const {
-    return (t.rt * 128 * cb + static_cast<int64_t>(t.cw) * 16) * 8;
   }
   __device__ __forceinline__ static int64_t place(uint32_t r, uint32_t c, uint32_t ctiles) {
     const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
@@ -125,16 +121,15 @@ struct SwizzledScales {
 // the count always completes.  The wait is bounded: past spin_limit sleeps the
 // workgroup goes on and marks the call failed with a NaN global scale.
 struct HeadGuard {
-  uint32_t* counters;  // null: no partials in q_out
-  int64_t bytes;       // head bytes holding partials and counters
-  uint32_t need;       // pass-2 workgroups
+  uint32_t* counters;  // null: no maxima in q_out
+  uint32_t need;       // quantize workgroups
   uint32_t spin_limit;
   float* gscale_out;
 };
 
 __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
   __shared__ int timed_out;
-  if (threadIdx.x < 64) {  // wave 0: one counter per lane
+  if (threadIdx.x < 64) {  // wave 0: one counter per lane (lanes past kCounters add 0)
     uint32_t spins = 0;
     int late = 0;
     // Each poll reads a counter with a fetch-and-add of zero: an atomic,
@@ -154,8 +149,10 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
     uint32_t zero = 0u;
     __asm__ volatile("" : "+v"(zero));
     for (;;) {
-      uint32_t c = __hip_atomic_fetch_add(h.counters + threadIdx.x * kCounterStride, zero, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t c = threadIdx.x < kCounters
+                       ? __hip_atomic_fetch_add(h.counters + threadIdx.x * kCounterStride, zero,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0u;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
       if (c >= h.need) break;
@@ -239,6 +236,26 @@ __device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, 
   // halves at [kThreads, 2 kThreads).  The destination operand is per wave:
   // lane l's 16 bytes land at slot 64 w + l, i.e. at threadIdx.x.
   // Address-space conversions take C-style casts.
+  const int w = threadIdx.x >> 6;
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(p), (lds_void_ptr)(pre + w * 64), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(pre + kThreads + w * 64), 16, 0,
+                                   0);
+}
+
+// Swizzled chunks: the lane's block of the first sub-iteration of the
+// workgroup's first chunk, loaded into LDS before the prologue (the pass has
+// no registers to spare for the row-major pass's early first-block load):
+// 16384 x 8192 swizzled step 101.3 -> 100.65 us, three A/B pairs.
+__device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x, int64_t nb,
+                                                  SwizzledScales smap, uint4* pre) {
+  const int64_t nchunks = smap.chunks(nb);
+  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  if (mine < 1) return;
+  int64_t b, si;
+  if (!smap.locate(smap.split(smap.order((mine - 1) * gridDim.x + blockIdx.x, nchunks)), 0, threadIdx.x, &b,
+                   &si))
+    return;
+  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
   const int w = threadIdx.x >> 6;
   __builtin_amdgcn_global_load_lds((global_void_ptr)(p), (lds_void_ptr)(pre + w * 64), 16, 0, 0);
   __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(pre + kThreads + w * 64), 16, 0,
@@ -343,53 +360,79 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
     __builtin_nontemporal_store(w, qc + threadIdx.x);
     (s + chunk * kThreads)[threadIdx.x] = static_cast<uint8_t>(sb);
   };
+  // With pass 1's maxima in q_out (head.counters set), chunk 0 holds them and
+  // chunk 1 the arrival counters: the workgroup that visits chunk 0 waits
+  // until every workgroup has counted itself in, writes chunk 0 and then
+  // chunk 1; the visitor of chunk 1 skips it.  Both chunks are whole there
+  // (the host takes that path from 512 blocks).  head_ok is uniform across
+  // the workgroup (wait_for_head synchronizes it).
+  auto head_ok = [&](int64_t chunk) -> bool {  // false: skip the chunk
+    if (!head.counters || chunk > 1) return true;
+    if (chunk == 1) return false;
+    wait_for_head(head);
+    return true;
+  };
+  auto head_tail = [&](int64_t chunk) {
+    if (head.counters && chunk == 0 && kThreads + threadIdx.x < nb) {
+      float lo[8], hi[8];
+      load_block(x + kThreads * 16, threadIdx.x, lo, hi);
+      finish(1, lo, hi);
+    }
+  };
   if (mine <= 0) return;
   {
     const int64_t chunk = smap.order((mine - 1) * gridDim.x + blockIdx.x, nchunks);
-    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
-    if (chunk * kThreads + threadIdx.x < nb) {
-      float lo[8], hi[8];
-      first.unpack(lo, hi);
-      finish(chunk, lo, hi);
+    if (head_ok(chunk)) {
+      if (chunk * kThreads + threadIdx.x < nb) {
+        float lo[8], hi[8];
+        first.unpack(lo, hi);
+        finish(chunk, lo, hi);
+      }
+      head_tail(chunk);
     }
   }
   int64_t it = mine - 2;
   if (PRE && prefetches_second(mine)) {  // the second chunk, from LDS (see prefetch_second)
     const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
-    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
-    if (chunk * kThreads + threadIdx.x < nb) {
-      float lo[8], hi[8];
-      widen8(pre[threadIdx.x], lo);
-      widen8(pre[kThreads + threadIdx.x], hi);
-      finish(chunk, lo, hi);
+    if (head_ok(chunk)) {
+      if (chunk * kThreads + threadIdx.x < nb) {
+        float lo[8], hi[8];
+        widen8(pre[threadIdx.x], lo);
+        widen8(pre[kThreads + threadIdx.x], hi);
+        finish(chunk, lo, hi);
+      }
+      head_tail(chunk);
     }
     --it;
   }
   for (; it >= 0; --it) {
     const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
-    if (head.counters && smap.first_q_byte(chunk) < head.bytes) wait_for_head(head);
+    if (!head_ok(chunk)) continue;
     if (chunk * kThreads + threadIdx.x < nb) {
       float lo[8], hi[8];
       load_block(x + chunk * kThreads * 16, threadIdx.x, lo, hi);
       finish(chunk, lo, hi);
     }
+    head_tail(chunk);
   }
 }
 
 // Pass 2 over swizzled chunks (see SwizzledScales), in the same order; the
 // chunk's scale tiles are assembled in LDS and stored whole.
-template <typename T, bool ROTATE, bool FAST, typename SMAP>
+template <typename T, bool ROTATE, bool FAST, typename SMAP, bool PRE>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
                                              const float2* __restrict__ tab,
                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                             SMAP smap, const HeadGuard& head) {
+                                             SMAP smap, const HeadGuard& head, const uint4* pre) {
+  // The swizzled layout never has pass 1's maxima in q_out: the host gives
+  // it the amax as one word (its head would span a whole row of tiles).
+  (void)head;
   const int64_t nchunks = smap.chunks(nb);
   const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const float rg = FAST ? 1.0f / g : 0.0f;
   __shared__ uint32_t stage[512];  // 4 scale tiles
   for (int64_t it = mine - 1; it >= 0; --it) {
     const auto tile = smap.split(smap.order(it * gridDim.x + blockIdx.x, nchunks));
-    if (head.counters && smap.first_q_byte(tile) < head.bytes) wait_for_head(head);
     for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
     __syncthreads();
 #pragma unroll 1
@@ -397,7 +440,12 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
       int64_t b, si;
       if (!smap.locate(tile, sub, threadIdx.x, &b, &si)) continue;
       float lo[8], hi[8];
-      load_block(x, b, lo, hi);
+      if (PRE && it == mine - 1 && sub == 0) {
+        widen8(pre[threadIdx.x], lo);
+        widen8(pre[kThreads + threadIdx.x], hi);
+      } else {
+        load_block(x, b, lo, hi);
+      }
       uint32_t sb;
       u32x2 w;
       encode_block<ROTATE, FAST>(lo, hi, g, rg, tab, &sb, &w);
@@ -429,10 +477,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   __shared__ uint32_t red[kThreads / 64];
   FirstBlock<T> first;
   if constexpr (!SMAP::kStaged) load_first(x, nb, smap, &first);  // staged: no registers to spare
-  constexpr bool kPre = !SMAP::kStaged && sizeof(T) == 2;
+  constexpr bool kPre = sizeof(T) == 2;
   __shared__ uint4 pre[kPre ? 2 : 1][kPre ? kThreads : 1];  // one element where unused
-  if constexpr (kPre) prefetch_second(x, nb, smap, &pre[0][0]);
-  HeadGuard head{nullptr, 0, 0, spin_limit, gscale_out};
+  if constexpr (kPre) {
+    if constexpr (SMAP::kStaged)
+      prefetch_first_sw(x, nb, smap, &pre[0][0]);
+    else
+      prefetch_second(x, nb, smap, &pre[0][0]);
+  }
+  HeadGuard head{nullptr, 0, spin_limit, gscale_out};
   uint32_t abits;
   if (npartials == 0) {
     abits = *amax_src;
@@ -445,7 +498,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     abits = red[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) abits = umax(abits, red[i]);
-    uint32_t* counters = const_cast<uint32_t*>(amax_src) + counter_base(npartials);
+    uint32_t* counters = const_cast<uint32_t*>(amax_src) + kCounterBase;
     // every thread's read of the partials is complete (their values met at
     // the barrier) before the workgroup counts itself in; a relaxed increment
     // needs no cache write-back
@@ -453,7 +506,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (blockIdx.x == 0 && threadIdx.x == 0) *amax_out = __uint_as_float(abits);
-    head = HeadGuard{counters, head_bytes(npartials), gridDim.x, spin_limit, gscale_out};
+    head = HeadGuard{counters, gridDim.x, spin_limit, gscale_out};
   }
   const float g = global_scale(__uint_as_float(abits));
   if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
@@ -467,14 +520,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       }
       __syncthreads();
       if constexpr (SMAP::kStaged)
-        quant_blocks<T, ROTATE, true>(x, nb, g, tab, q, s, smap, head);
+        quant_blocks<T, ROTATE, true, SMAP, kPre>(x, nb, g, tab, q, s, smap, head, &pre[0][0]);
       else
         quant_blocks_rm<T, ROTATE, true, kPre>(x, nb, g, tab, q, s, smap, head, first, &pre[0][0]);
       return;
     }
   }
   if constexpr (SMAP::kStaged)
-    quant_blocks<T, ROTATE, false>(x, nb, g, tab, q, s, smap, head);
+    quant_blocks<T, ROTATE, false, SMAP, kPre>(x, nb, g, tab, q, s, smap, head, &pre[0][0]);
   else
     quant_blocks_rm<T, ROTATE, false, kPre>(x, nb, g, tab, q, s, smap, head, first, &pre[0][0]);
 }

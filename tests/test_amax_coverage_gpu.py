@@ -72,7 +72,7 @@ def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
 @pytest.mark.parametrize("rows,cols,calls", [(16384, 8192, 400), (2048, 8192, 2000), (4096, 4096, 2000)])
 def test_repeated_calls_keep_the_global_scale(nv, monkeypatch, rows, cols, calls):
     """Back-to-back fused calls on one set of buffers: every call's amax and
-    global scale equal the oracle's.  A quantize workgroup that writes over the
+    global scale equal the oracle's.  The quantize workgroup that writes the
     head of q_out first waits for every workgroup to have read pass 1's maxima
     there; a wait that ran out would leave a NaN global scale."""
     monkeypatch.delenv("NVFP4RQ_AMAX_WGS", raising=False)

@@ -644,12 +644,12 @@ def test_given_scale_and_decode_at_bench_size(nv):
     assert np.all(err <= 1e-6 * np.abs(yd).reshape(-1, 16).max(1, keepdims=True))
 
 
-@pytest.mark.parametrize("nb", [1039, 1040, 1041, 2047, 2048, 2049, 4101])
+@pytest.mark.parametrize("nb", [511, 512, 513, 767, 1040, 2047, 2048, 2049, 4101])
 def test_partials_path_threshold(nv, monkeypatch, nb):
     """Around the size from which pass 1's maxima and counters fit at the head
-    of q_out (about 1040 blocks), in one row and in one column of blocks, with
-    the default grid and with pass-2 grids of 1 and 7 workgroups (one
-    workgroup then owns every chunk that overlaps the head)."""
+    of q_out (512 blocks: chunks 0 and 1, written by chunk 0's workgroup alone),
+    in one row and in one column of blocks, with the default grid and with
+    pass-2 grids of 1 and 7 workgroups."""
     for rows, cols in ((1, 16 * nb), (nb, 16)):
         x = mixed_input(rows, cols, "bf16", seed=nb + rows)
         xd = to_dev(x)

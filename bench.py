@@ -56,12 +56,41 @@ def algorithmic_bytes(n_elem: int, in_bytes: int) -> dict:
     }
 
 
+def code_tokens(src: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so that
+    editing a comment leaves the hash below unchanged (string and character
+    literals are kept whole)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources' code (comments and layout ignored): the
+    committed counter summaries are used only while it matches theirs."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_activation_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(f.encode() + b"\0")
+            h.update(code_tokens(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

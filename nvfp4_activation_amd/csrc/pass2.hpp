@@ -113,13 +113,15 @@ struct SwizzledScales {
   }
 };
 
-// When pass 1 leaves its per-workgroup maxima at the head of q_out, every
-// pass-2 workgroup reads them in its prologue and then counts itself in; a
-// workgroup waits for all of them to have done so before it writes a chunk
-// whose codes reach into that head.  Chunks run last-first, so the wait comes
-// at the end of the few workgroups concerned, and since the others never wait
-// the count always completes.  The wait is bounded: past spin_limit sleeps the
-// workgroup goes on and marks the call failed with a NaN global scale.
+// When pass 1 leaves its per-workgroup maxima at the head of q_out (chunk 0,
+// with the arrival counters in chunk 1), every pass-2 workgroup reads them in
+// its prologue and then counts itself in.  One workgroup alone, the one that
+// draws chunk 0, waits for all of them to have done so and then writes both
+// head chunks; nobody else waits, so the count always completes, and no
+// counter is written over while another workgroup still reads it.  Chunks run
+// last-first, so that wait comes at the end of its workgroup.  It is bounded:
+// past spin_limit sleeps the workgroup goes on and marks the call failed with
+// a NaN global scale.
 struct HeadGuard {
   uint32_t* counters;  // null: no maxima in q_out
   uint32_t need;       // quantize workgroups
@@ -133,13 +135,8 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
     uint32_t spins = 0;
     int late = 0;
     // Each poll reads a counter with a fetch-and-add of zero: an atomic,
-    // performed where the increments are performed.  A relaxed agent-scope
-    // load (global_load sc1) may instead be answered by the XCD's own L2,
-    // which can still hold the line as the amax pass's clearing store left it
-    // on XCD 0, where most waiters run; once streaming traffic stops evicting
-    // that line, such a waiter saw a stale sum until its spin limit ran out
-    // (a few calls in 10^4 at 4096 x 4096 with a 48-workgroup amax pass).
-    // Relaxed ordering: acquire/release at agent scope would write back or
+    // performed where the increments are performed, so no copy of the line
+    // in another cache can answer it.  Relaxed ordering: acquire/release at agent scope would write back or
     // invalidate the L2 of every XCD involved on each poll.  Nothing written
     // by other workgroups is read after the wait; the waiter's stores follow
     // the loop.

@@ -21,6 +21,9 @@
  * value t, every y within `w` ulps of RN(d * t).  Every case is compared bit
  * for bit with C's binary32 division (IEEE round to nearest even).
  *
+ * The element quotients use a two-operation form instead (verify_element2,
+ * verify_random_codes2 below): exact codes, not exact quotients.
+ *
  * Test code: built and run by tests/test_fastdiv_cpu.py.
  */
 #include <math.h>
@@ -108,16 +111,18 @@ long long verify_block(int w, uint32_t *ex_g, uint32_t *ex_a)
     return bad;
 }
 
-/* a / 6 with the constant r6 = RN(1/6), every positive binary32 in [lo, hi] */
-long long verify_div6(uint32_t lo, uint32_t hi, uint32_t *ex)
+/* a / c with the constant r = RN(1/c), every positive binary32 in [lo, hi]
+   (c = 6: the block value of an unrotated block; c = 24: of a rotated one,
+   whose butterfly output z = 4y enters unscaled, z / 24 = y / 6 exactly) */
+long long verify_div_const(float c, uint32_t lo, uint32_t hi, uint32_t *ex)
 {
-    const float r6 = 1.0f / 6.0f;
+    const float r = 1.0f / c;
     long long bad = 0;
     uint32_t b = 0;
 #pragma omp parallel for schedule(static) reduction(+ : bad)
     for (int64_t u = lo; u <= (int64_t)hi; u++) {
         float a = fbits((uint32_t)u);
-        if (bitsf(a / 6.0f) != bitsf(mk(a, 6.0f, r6))) {
+        if (bitsf(a / c) != bitsf(mk(a, c, r))) {
             bad++;
 #pragma omp critical
             b = (uint32_t)u;
@@ -193,5 +198,135 @@ long long verify_random_codes(int64_t n, uint64_t seed, double *max_ulp_seen)
         }
     }
     *max_ulp_seen = mx;
+    return bad;
+}
+
+/*
+ * Two-operation element quotient.  Once per divisor D (per scale byte, in a
+ * table): rh = RN(1/D); e = RN(1 - rh D), exact as one fma; rl = RN(e / D),
+ * a correctly rounded division.  Per element: p = RN(z rl + 0) (fma with +0,
+ * so that a zero z gives +0), q = RN(z rh + p) (fma).
+ *
+ * rh + rl equals 1/D within about 2^-47 relative, and p adds an error below
+ * 2^-48 of the quotient, so q = RN(Q (1 + eps)) with |eps| < 2^-46 and
+ * Q = z / D exactly: q is RN(Q) or an adjacent binary32, and its E2M1 code can
+ * differ from that of RN(Q) only where Q lies within about two ulps of one of
+ * the seven midpoints.  verify_element2 enumerates exactly those inputs, for
+ * every significand of D, and compares codes (the quotient bits may differ
+ * by an ulp away from a midpoint; the code never does).  Rounding is
+ * invariant under a common power-of-two scaling of z and D while nothing
+ * under- or overflows, which holds for the tables the kernels build (D in
+ * [2^-57, 2^15): rl is a normal number and z rl stays far from the underflow
+ * threshold wherever Q is near a midpoint; a nonzero z, a multiple of
+ * 2^-133, gives |Q| >= 2^-148, so q is never a zero of the wrong sign).
+ *
+ * The tail must be the correctly rounded e / D: with RN(e rh) instead,
+ * D = 8 (1 - 2^-24) and z = 2 give rh + rl = (1 + 2^-24) / 8 exactly, so that
+ * Q = 0.25 (1 + 2^-24 + 2^-48 + ...), just above the rounding boundary
+ * between 0.25 and its successor, is approximated by the boundary itself and
+ * rounds (to even) to 0.25: code 0 instead of 1.
+ */
+static inline void recip2(float d, float *rh, float *rl)
+{
+    float r = 1.0f / d;
+    float e = fmaf(-r, d, 1.0f);
+    *rh = r;
+    *rl = e / d;
+}
+
+static inline float q2(float z, float rh, float rl)
+{
+    float p = fmaf(z, rl, 0.0f);
+    return fmaf(z, rh, p);
+}
+
+long long verify_element2(int w, uint32_t *ex_d, uint32_t *ex_z)
+{
+    static const float T[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    long long bad = 0;
+    uint32_t bd = 0, bz = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t D = 0; D < (1 << 23); D++) {
+        float d4 = 4.0f * fbits(0x3F800000u | (uint32_t)D);
+        float rh, rl;
+        recip2(d4, &rh, &rl);
+        for (int k = 0; k < 7; k++) {
+            uint32_t cb = bitsf(d4 * T[k]);
+            for (int j = -w; j <= w; j++) {
+                float z = fbits(cb + (uint32_t)j);
+                for (int sg = 0; sg < 2; sg++) {
+                    float zz = sg ? -z : z;
+                    float got = q2(zz, rh, rl);
+                    if (code_of(zz / d4) != code_of(got)) {
+                        bad++;
+#pragma omp critical
+                        { bd = bitsf(d4); bz = bitsf(zz); }
+                    }
+                }
+            }
+        }
+    }
+    *ex_d = bd;
+    *ex_z = bz;
+    return bad;
+}
+
+/* Largest |(rh + rl) D - 1| over every significand of D, in units of 2^-48
+   (extended precision; the argument above needs it below 2). */
+double max_tail_error(void)
+{
+    double mx = 0.0;
+#pragma omp parallel for schedule(static) reduction(max : mx)
+    for (int64_t D = 0; D < (1 << 23); D++) {
+        float d = fbits(0x3F800000u | (uint32_t)D);
+        float rh, rl;
+        recip2(d, &rh, &rl);
+        long double err = fabsl(((long double)rh + (long double)rl) * (long double)d - 1.0L);
+        double u = (double)(err * 0x1p48L);
+        if (u > mx)
+            mx = u;
+    }
+    return mx;
+}
+
+/*
+ * Random pairs over the whole range the kernels allow, as verify_random_codes
+ * but for the two-operation quotient: the code of q (a zero must come out as
+ * +0, which the sign rule gives code 0) equals the code of RN(z / D).
+ */
+long long verify_random_codes2(int64_t n, uint64_t seed)
+{
+    long long bad = 0;
+#pragma omp parallel reduction(+ : bad)
+    {
+        uint64_t s = seed * 0x632be59bd9b4e019ULL + 1;
+#ifdef _OPENMP
+        extern int omp_get_thread_num(void);
+        s += (uint64_t)omp_get_thread_num() * 0x9e3779b97f4a7c15ULL * 7;
+#endif
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; i++) {
+            uint64_t a = sm64(&s), b = sm64(&s);
+            int de = -60 + (int)(a % 76);   /* D in [2^-60, 2^16) */
+            float d4 = ldexpf(1.0f + (float)((a >> 8) & 0x7FFFFF) / 8388608.0f, de);
+            float rh, rl;
+            recip2(d4, &rh, &rl);
+            float z;
+            int kind = (int)(b & 7);
+            if (kind < 6) {
+                z = (float)((double)d4 * 6.5 * ((double)(b >> 11) * 0x1.0p-53));
+            } else {
+                int ze = -133 + (int)((b >> 3) % 140);
+                z = ldexpf((float)((b >> 11) & 0xFFFF) / 65536.0f + 1.0f, ze);
+            }
+            if ((b >> 63) & 1)
+                z = -z;
+            if (fabsf(z) < 0x1p-133f)
+                z = ((b >> 62) & 1) ? -0.0f : 0.0f;
+            float got = q2(z, rh, rl);
+            if (code_of(z / d4) != code_of(got) || (got == 0.0f && signbit(got)))
+                bad++;
+        }
+    }
     return bad;
 }

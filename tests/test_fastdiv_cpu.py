@@ -1,12 +1,17 @@
-"""CPU proof that the kernels' division shortcut is exact where it is used.
+"""CPU proof that the kernels' division shortcuts are exact where they are used.
 
 The rotate+quantize kernel replaces each binary32 division y / d of the
 definition (page "A Fused Hadamard + NVFP4 Quantization Kernel in Triton",
-section 2: the block value (amax / 6) / g and the element quotient) by a
-reciprocal computed once with a true division and a fused-multiply-add
-correction (Markstein).  These enumerations show it returns the correctly
-rounded quotient at every input that can change an E2M1 code or an E4M3
-scale (see tests/helpers/fastdiv.c for the argument).
+section 2: the block value (amax / 6) / g and the element quotient) by
+multiplications with reciprocals computed once with true divisions:
+
+- the block value: a fused-multiply-add correction (Markstein), which returns
+  the correctly rounded quotient at every input that can change an E4M3 scale;
+- the element quotient: a two-word reciprocal (two fused multiply-adds per
+  element), whose E2M1 code equals that of the correctly rounded quotient at
+  every input where the two could differ.
+
+See tests/helpers/fastdiv.c for the arguments.
 """
 from __future__ import annotations
 
@@ -31,8 +36,14 @@ def lib(tmp_path_factory):
     lib.verify_element.restype = ctypes.c_longlong
     lib.verify_block.argtypes = [ctypes.c_int, u32p, u32p]
     lib.verify_block.restype = ctypes.c_longlong
-    lib.verify_div6.argtypes = [ctypes.c_uint32, ctypes.c_uint32, u32p]
-    lib.verify_div6.restype = ctypes.c_longlong
+    lib.verify_div_const.argtypes = [ctypes.c_float, ctypes.c_uint32, ctypes.c_uint32, u32p]
+    lib.verify_div_const.restype = ctypes.c_longlong
+    lib.verify_element2.argtypes = [ctypes.c_int, u32p, u32p]
+    lib.verify_element2.restype = ctypes.c_longlong
+    lib.max_tail_error.argtypes = []
+    lib.max_tail_error.restype = ctypes.c_double
+    lib.verify_random_codes2.argtypes = [ctypes.c_int64, ctypes.c_uint64]
+    lib.verify_random_codes2.restype = ctypes.c_longlong
     lib.verify_random_codes.argtypes = [ctypes.c_int64, ctypes.c_uint64,
                                         ctypes.POINTER(ctypes.c_double)]
     lib.verify_random_codes.restype = ctypes.c_longlong
@@ -51,15 +62,17 @@ def test_block_value_at_every_e4m3_boundary(lib):
     assert bad == 0, f"{bad} mismatches, e.g. g={a.value:#010x} a={b.value:#010x}"
 
 
-def test_divide_by_six_every_float(lib):
-    """Exact for every binary32 from 2^-124 up.  Below that the remainder
-    underflows; such a block value is below 2^-70 once divided by a global
-    scale >= 2^-52 (the kernels' fast-path range), so its E4M3 scale is 0
-    whichever way the quotient rounds."""
+@pytest.mark.parametrize("c,lo", [(6.0, 0x01800000), (24.0, 0x02800000)])
+def test_divide_by_constant_every_float(lib, c, lo):
+    """a / 6 exact for every binary32 from 2^-124 up, a / 24 from 2^-122 up
+    (the rotated block's amax enters unscaled, z / 24 = y / 6).  Below that
+    the remainder underflows; such a block value is below 2^-70 once divided
+    by a global scale >= 2^-52 (the kernels' fast-path range), so its E4M3
+    scale is 0 whichever way the quotient rounds."""
     a = ctypes.c_uint32()
-    bad = lib.verify_div6(0x01800000, 0x7F7FFFFF, ctypes.byref(a))
+    bad = lib.verify_div_const(c, lo, 0x7F7FFFFF, ctypes.byref(a))
     assert bad == 0, f"{bad} mismatches, e.g. bits {a.value:#010x}"
-    bad_low = lib.verify_div6(1, 0x017FFFFF, ctypes.byref(a))
+    bad_low = lib.verify_div_const(c, 1, lo - 1, ctypes.byref(a))
     assert bad_low > 0   # the underflow region is real; the range above is what is proved
 
 
@@ -67,3 +80,22 @@ def test_random_element_codes(lib):
     mx = ctypes.c_double()
     bad = lib.verify_random_codes(200_000_000, 12345, ctypes.byref(mx))
     assert bad == 0, f"{bad} code mismatches (max ulp difference {mx.value})"
+
+
+def test_two_word_reciprocal_tail(lib):
+    """rh + rl approximates 1/D within 2^-47 relative for every significand,
+    the bound the window argument for the two-operation quotient rests on."""
+    assert lib.max_tail_error() < 2.0
+
+
+def test_element_codes_two_operation_quotient(lib):
+    """Every input within 16 ulps of every E2M1 decision boundary, both signs,
+    for all 2^23 divisor significands: the two-operation quotient gives the
+    code of the correctly rounded one."""
+    a, b = ctypes.c_uint32(), ctypes.c_uint32()
+    bad = lib.verify_element2(16, ctypes.byref(a), ctypes.byref(b))
+    assert bad == 0, f"{bad} mismatches, e.g. D={a.value:#010x} z={b.value:#010x}"
+
+
+def test_random_element_codes_two_operation_quotient(lib):
+    assert lib.verify_random_codes2(200_000_000, 777) == 0

@@ -46,7 +46,8 @@
  *   - Outputs must not overlap the input or each other (NVFP4_ERR_ARG).
  *   - Calls that share an output buffer must be ordered (same stream or
  *     explicit events): the amax word can be an atomic accumulator, and the
- *     fused call keeps pass 1's partial maxima at the head of q_out.
+ *     fused calls keep pass 1's partial maxima at the head of q_out (or of
+ *     s_out for the swizzled layout).
  *   - No C++ exception crosses this interface.
  */
 #ifndef NVFP4RQ_H
@@ -90,13 +91,17 @@ typedef enum nvfp4_status {
  *               scales (0x00..0x7E), row-major [rows, cols/16].  May be NULL
  *               when rows * cols == 0.
  *   gscale_out  device, 1 float, 4-byte aligned: the global scale s_global.
- *               NaN if the quantize pass gave up waiting for its own
- *               workgroups (a bounded wait that cannot run out while the
- *               device schedules the grid).
  *   amax_out    device, 1 float, 4-byte aligned: the rotated global amax.
  *               Written by this call (for small tensors it is zeroed and
  *               used as the pass-1 accumulator).
  *   stream      HIP stream.
+ * Failure mark: with the maxima at the head of q_out, one quantize
+ * workgroup writes the head last, after a wait for every workgroup to have
+ * read them.  That wait is bounded (200 ms of device wall clock; it cannot
+ * run out while the device runs the grid, only if other work keeps part of
+ * the grid from starting that long).  If it runs out, gscale_out and
+ * amax_out are NaN and every output of the call (codes and scales too) is
+ * invalid; the status is still NVFP4_OK, since nothing is read back.
  * rows * cols == 0 is valid: it writes amax 0 and global scale 1.
  */
 nvfp4_status nvfp4_rotquant(const uint16_t *x_bf16, int64_t rows, int64_t cols, int rotate,
@@ -192,10 +197,16 @@ nvfp4_status nvfp4_rotquant_f32_timed(const float *x, int64_t rows, int64_t cols
  * 512*(rt*ceil(cols/64) + ct) + 16*j + 4*i + k.
  *
  * nvfp4_swizzled_scale_bytes: size of that buffer, 512*ceil(rows/128)*
- * ceil(cols/64); -1 for a bad shape or more than 2^32 - 1 blocks.
+ * ceil(cols/64); -1 for a bad shape or more than 2^32 - 1 blocks.  The
+ * quantize calls also need 128 rows of input below 2^31 bytes (cols < 2^23
+ * for bf16, < 2^22 for fp32; NVFP4_ERR_SHAPE otherwise).
  * nvfp4_rotquant_swizzled(_f32): nvfp4_rotquant with s_out in this layout
  * (s_out holds nvfp4_swizzled_scale_bytes bytes, 4-byte aligned; padding bytes
- * are written as 0).  Codes, g and amax are as for nvfp4_rotquant.
+ * are written as 0).  Codes, g and amax are as for nvfp4_rotquant.  When a
+ * row holds at least 8 scale tiles (cols >= 464) and two column windows of
+ * 16 blocks, the call keeps pass 1's per-workgroup maxima and arrival
+ * counters in the first 4 KiB of s_out instead of q_out, with the same
+ * failure mark; s_out is then defined only once the call has completed.
  * nvfp4_dequant_swizzled: nvfp4_dequant reading scales in this layout.
  */
 int64_t nvfp4_swizzled_scale_bytes(int64_t rows, int64_t cols);
@@ -278,7 +289,6 @@ nvfp4_status mxfp4_rotquant_f32(const float *x, int64_t rows, int64_t cols, int 
 nvfp4_status mxfp4_dequant(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols,
                            int rotate, float *y_out, hipStream_t stream);
 
-/* Static English text for a status code; never NULL. */
 /*
  * Measurement support, not part of the method: the launch sequence of
  * nvfp4_rotquant (or _f32) for the same tensor, with each pass replaced by a
@@ -296,6 +306,7 @@ nvfp4_status nvfp4_stream_calibrate(const uint16_t *x_bf16, int64_t rows, int64_
 nvfp4_status nvfp4_stream_calibrate_f32(const float *x, int64_t rows, int64_t cols,
                                         uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
 
+/* Static English text for a status code; never NULL. */
 const char *nvfp4_status_string(nvfp4_status status);
 
 #ifdef __cplusplus

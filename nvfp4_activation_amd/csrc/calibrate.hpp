@@ -65,31 +65,30 @@ __global__ __launch_bounds__(kThreads) void stream_read_f32_kernel(const float* 
   workgroup_max_to(m, out, partials);
 }
 
-// Twin of rotquant_kernel with row-major scales: the same chunk order; each
-// lane loads its block, stores 8 bytes non-temporally where its codes go and
-// one byte where its scale goes.
+// Twin of rotquant_kernel with row-major scales: the same chunk order and
+// raw buffer accesses; each lane loads its block, stores 8 bytes
+// non-temporally where its codes go and one byte where its scale goes.
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void stream_rw_kernel(
-    const T* __restrict__ x, int64_t nb, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-    RowMajorScales smap) {
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
-  for (int64_t it = mine - 1; it >= 0; --it) {
-    const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
-    int64_t b, si;
-    if (!smap.locate(chunk, 0, threadIdx.x, nb, &b, &si)) continue;
-    const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
+    const T* __restrict__ x, int64_t nb, uint8_t* q, uint8_t* s, RowMajorScales smap, Launch vis) {
+  const uint32_t nchunks = vis.nchunks;
+  const uint32_t nfull = static_cast<uint32_t>(nb / kThreads);
+  const uint32_t tail = static_cast<uint32_t>(nb % kThreads);
+  const uint32_t mine = vis.of(blockIdx.x);
+  for (int32_t it = static_cast<int32_t>(mine) - 1; it >= 0; --it) {
+    const uint32_t chunk = smap.order(static_cast<uint32_t>(it) * vis.grid + blockIdx.x, nchunks);
+    const uint32_t valid = chunk < nfull ? kThreads : tail;
+    Block<T> blk;
+    blk.load(x, chunk, valid, threadIdx.x);
     uint32_t w0, w1;
     if constexpr (sizeof(T) == 2) {
-      w0 = fold(p[0]);
-      w1 = fold(p[1]);
+      w0 = blk.a.x ^ blk.a.y ^ blk.a.z ^ blk.a.w;
+      w1 = blk.b.x ^ blk.b.y ^ blk.b.z ^ blk.b.w;
     } else {
-      w0 = fold(p[0]) ^ fold(p[1]);
-      w1 = fold(p[2]) ^ fold(p[3]);
+      w0 = blk.a.x ^ blk.a.y ^ blk.a.z ^ blk.a.w ^ blk.b.x ^ blk.b.y ^ blk.b.z ^ blk.b.w;
+      w1 = blk.c.x ^ blk.c.y ^ blk.c.z ^ blk.c.w ^ blk.d.x ^ blk.d.y ^ blk.d.z ^ blk.d.w;
     }
-    const u32x2 w = {w0, w1};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(q + b * 8));
-    s[si] = static_cast<uint8_t>(w0 ^ w1);
+    store_chunk_block(q, s, chunk, valid, threadIdx.x, u32x2{w0, w1}, w0 ^ w1);
   }
 }
 

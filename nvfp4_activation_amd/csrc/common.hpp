@@ -61,12 +61,12 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 // 4096 x 4096: 21.4 -> 20.2 us).  A bijection when the grid is a multiple of
 // 16; other grids keep b.
 static_assert(kAmaxPieces == 4, "pass1_wg pairs workgroups of two chunks each");
-__device__ __forceinline__ int64_t pass1_wg() {
-  const int64_t b = blockIdx.x;
-  if (gridDim.x % 16 != 0) return b;
+__host__ __device__ inline int64_t pass1_wg_of(int64_t b, int64_t grid) {
+  if (grid % 16 != 0) return b;
   const int64_t j = b >> 3;
   return 16 * (j >> 1) + 2 * (b & 7) + (j & 1);
 }
+__device__ __forceinline__ int64_t pass1_wg() { return pass1_wg_of(blockIdx.x, gridDim.x); }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
 #pragma unroll

@@ -91,6 +91,22 @@ int device_cus() {
   return c;
 }
 
+// Ticks of the device's constant-rate wall clock (the clock wall_clock64
+// reads) per millisecond, cached per device; 100 MHz if the runtime does not
+// say.
+int64_t wall_ticks_per_ms() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100000;
+  int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeWallClockRate, dev) != hipSuccess || c <= 0)
+      c = 100000;  // kHz
+    __atomic_store_n(&cache[dev], c, __ATOMIC_RELAXED);
+  }
+  return c;
+}
+
 // Positive integer from the environment, or 0.  Used to override launch
 // shapes in tests (results never depend on them).
 int64_t env_int(const char* name) {
@@ -172,6 +188,8 @@ nvfp4_status check_shape(int64_t rows, int64_t cols, int64_t* nb) {
   // largest buffer is rows * cols * 4 bytes (fp32 input or output)
   if (cols != 0 && rows > (INT64_MAX / 8) / cols) return NVFP4_ERR_SHAPE;
   *nb = rows * (cols / 16);
+  // the quantize pass counts 256-block chunks in 32 bits
+  if (*nb >= (int64_t{1} << 39)) return NVFP4_ERR_SHAPE;
   return NVFP4_OK;
 }
 
@@ -243,36 +261,54 @@ nvfp4_status enqueue_rotamax(const T* x, int64_t nb, int rotate, float* amax, hi
   return launch_rotamax(x, nb, rotate, bits, 0, st) == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-// Pass 2.  npartials == 0: the amax is the word at amax_src.  Otherwise
-// amax_src holds npartials per-workgroup maxima and the counter (at the head
-// of q) and the kernel writes their maximum to amax_out.
-template <typename T, typename SMAP = RowMajorScales>
-nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, const uint32_t* amax_src,
-                           int npartials, float* amax_out, uint8_t* q, uint8_t* s, float* g,
-                           hipStream_t st, SMAP smap = SMAP{}) {
+// The quantize pass's head wait gives up after this long (see HeadGuard):
+// far beyond any wait a scheduled grid needs (the waiting workgroup starts
+// waiting once its own chunks are done, when every other workgroup has long
+// counted itself in), short enough that a failure shows within a fraction of
+// a second.  NVFP4RQ_HEAD_TIMEOUT_US overrides it (tests).
+constexpr int64_t kHeadTimeoutMs = 200;
+uint64_t head_ticks() {
+  const int64_t us = env_int("NVFP4RQ_HEAD_TIMEOUT_US");
+  const int64_t per_ms = wall_ticks_per_ms();
+  return static_cast<uint64_t>(us > 0 ? per_ms * us / 1000 : per_ms * kHeadTimeoutMs);
+}
+
+// Pass 2.  MODE kWord / kGiven: the amax is the word at amax_src (written by
+// pass 1 on the same tensor, or kept from elsewhere).  kHead: amax_src holds
+// npartials per-workgroup maxima and the counters (at the head of q or s) and
+// the kernel writes their maximum to amax_out.
+template <typename T, AmaxMode MODE, typename SMAP = RowMajorScales>
+nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_src, int npartials,
+                           float* amax_out, uint8_t* q, uint8_t* s, float* g, hipStream_t st,
+                           SMAP smap = SMAP{}) {
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
   const int64_t nchunks = smap.chunks(nb);
   dim3 grid(quant_grid(nchunks * kThreads));
-  if (npartials == 0) {
+  if constexpr (MODE != kHead) {
     // Amax given as a word: the workgroup prologue is a single load, and a
     // workgroup per chunk beats 8 persistent ones per CU (16384 x 8192 bf16,
     // cold: 62 against 68 us); with per-workgroup maxima to reduce first,
     // the persistent grid stays ahead.
     grid = dim3(clamp_grid(nchunks, nchunks));
     smap.mirror = 1;
-  } else if constexpr (std::is_same_v<SMAP, RowMajorScales> && sizeof(T) == 2) {
-    // bf16: runs of 4 consecutive chunks per XCD (see RowMajorScales::order).
-    // fp32 chunks (16 KiB) do best in plain order: at 65536 x 1024 the step
-    // took 91.1 us against 92.7 with runs of 4 or 8.
-    smap.xcd_order = nchunks % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
+  } else {
+    // workgroup 0 visits both head chunks (head_order): the grid leaves it two
+    // visits
+    if (grid.x > nchunks - 1) grid.x = static_cast<unsigned>(nchunks - 1);
+    if constexpr (std::is_same_v<SMAP, RowMajorScales> && sizeof(T) == 2) {
+      // bf16: runs of 4 consecutive chunks per XCD (see RowMajorScales::order).
+      // fp32 chunks (16 KiB) do best in plain order: at 65536 x 1024 the step
+      // took 91.1 us against 92.7 with runs of 4 or 8.
+      smap.xcd_order = nchunks % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
+    }
   }
-  const int64_t spin_env = env_int("NVFP4RQ_SPIN_LIMIT");
-  const uint32_t spin_limit = spin_env > 0 ? static_cast<uint32_t>(spin_env) : (1u << 26);
+  const Launch vis = Launch::make(static_cast<uint32_t>(nchunks), grid.x, allow_fast);
+  const uint64_t ticks = head_ticks();
   const hipError_t e =
-      rotate ? launch(rotquant_kernel<T, true, SMAP>, grid, dim3(kThreads), st, x, nb, amax_src,
-                      npartials, amax_out, spin_limit, allow_fast, q, s, g, smap)
-             : launch(rotquant_kernel<T, false, SMAP>, grid, dim3(kThreads), st, x, nb, amax_src,
-                      npartials, amax_out, spin_limit, allow_fast, q, s, g, smap);
+      rotate ? launch(rotquant_kernel<T, true, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
+                      npartials, amax_out, ticks, q, s, g, smap, vis)
+             : launch(rotquant_kernel<T, false, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
+                      npartials, amax_out, ticks, q, s, g, smap, vis);
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
@@ -280,18 +316,34 @@ bool zeroed_word_path(int g1, int64_t nb, bool large) {
   return g1 > kMaxPartials || kHeadBytes > 8 * nb || large || env_int("NVFP4RQ_ZEROED_AMAX");
 }
 
-// Both passes.  When q_out has room (8 nb bytes against kHeadBytes: from 512
-// blocks up) and pass 1 has at most kMaxPartials workgroups, pass 1 leaves
-// per-workgroup maxima and cleared counters at the head of q_out (which one
-// pass-2 workgroup overwrites last), so no word has to be zeroed first;
-// smaller tensors, wider pass-1 grids and the swizzled layout take the
-// zeroed-word path.  So do row-major
-// inputs of kOneShotInputBytes and more: with the amax in one word, pass 2
-// runs a workgroup per chunk, which streams inputs well past the last-level
-// cache faster than the persistent grid that the per-workgroup maxima call
-// for (bf16, 14336 columns, step with the zeroing kernel included: 470 MB
-// input even, 587 MB 2.5% faster, 705 MB 3.3%, 939 MB 5.5%; below about
-// 470 MB the persistent grid's cache reuse wins, 268 MB by 7%).
+// Where pass 1 can leave its per-workgroup maxima and the arrival counters:
+// the first kHeadBytes of q_out (row-major: chunks 0 and 1 of the codes),
+// or of s_out for the swizzled layout (the scale tiles of chunks 0 and 1,
+// which are 2 KiB each and consecutive when a row of blocks spans at least
+// 8 tiles, cols >= 464 and ctiles >= 8, and there is a second column
+// window).  A swizzled chunk is 2048 blocks; below kSwizzledHeadChunks of
+// them the one-word path's grid of one workgroup per chunk is faster than
+// a head writer with two chunks to itself (128 x 1024, 4 chunks: 21.6 us
+// against 18.9 us per step).
+constexpr int64_t kSwizzledHeadChunks = 32;
+uint32_t* head_of(uint8_t* q, uint8_t*, int64_t, RowMajorScales) { return reinterpret_cast<uint32_t*>(q); }
+uint32_t* head_of(uint8_t*, uint8_t* s, int64_t nb, const SwizzledScales& sm) {
+  return sm.ctiles >= 8 && sm.cs >= 2 && sm.chunks(nb) >= kSwizzledHeadChunks ? reinterpret_cast<uint32_t*>(s)
+                                                                                : nullptr;
+}
+
+// Both passes.  When the head has room (row-major: 8 nb bytes of codes
+// against kHeadBytes, from 512 blocks up; swizzled: see head_of) and pass 1
+// has at most kMaxPartials workgroups, pass 1 leaves per-workgroup maxima
+// and cleared counters there (which one pass-2 workgroup overwrites last), so
+// no word has to be zeroed first; other tensors and wider pass-1 grids take
+// the zeroed-word path.  So do row-major inputs of kOneShotInputBytes and
+// more: with the amax in one word, pass 2 runs a workgroup per chunk, which
+// streams inputs well past the last-level cache faster than the persistent
+// grid that the per-workgroup maxima call for (bf16, 14336 columns, step with
+// the zeroing kernel included: 470 MB input even, 587 MB 2.5% faster, 705 MB
+// 3.3%, 939 MB 5.5%; below about 470 MB the persistent grid's cache reuse
+// wins, 268 MB by 7%).
 template <typename T, typename SMAP = RowMajorScales>
 nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_t* s, float* g,
                           float* amax, hipStream_t st, SMAP smap = SMAP{}) {
@@ -300,16 +352,15 @@ nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_
   // per step at 939 MB)
   const bool large = std::is_same_v<SMAP, RowMajorScales> &&
                      nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
-  // The swizzled layout always takes the amax as one word (see quant_blocks).
-  if (nb == 0 || !std::is_same_v<SMAP, RowMajorScales> || zeroed_word_path(g1, nb, large)) {
+  uint32_t* head = head_of(q, s, nb, smap);
+  if (nb == 0 || !head || zeroed_word_path(g1, nb, large)) {
     nvfp4_status r = enqueue_rotamax(x, nb, rotate, amax, st);
     if (r != NVFP4_OK) return r;
-    return enqueue_quant(x, nb, rotate, reinterpret_cast<const uint32_t*>(amax), 0, amax, q, s, g, st,
-                         smap);
+    return enqueue_quant<T, kWord>(x, nb, rotate, reinterpret_cast<uint32_t*>(amax), 0, amax, q, s, g, st,
+                                   smap);
   }
-  uint32_t* head = reinterpret_cast<uint32_t*>(q);
   if (launch_rotamax(x, nb, rotate, head, 1, st) != hipSuccess) return NVFP4_ERR_HIP;
-  return enqueue_quant(x, nb, rotate, head, g1, amax, q, s, g, st, smap);
+  return enqueue_quant<T, kHead>(x, nb, rotate, head, g1, amax, q, s, g, st, smap);
 }
 
 // Measurement support (calibrate.hpp): the fused call's launch sequence for
@@ -354,7 +405,9 @@ nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q
     if constexpr (sizeof(T) == 2)
       smap.xcd_order = nchunks % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
   }
-  return launch(stream_rw_kernel<T>, grid, dim3(kThreads), st, x, nb, q, s, smap) == hipSuccess
+  if (!zeroed_word_path(g1, nb, large) && grid.x > nchunks - 1) grid.x = static_cast<unsigned>(nchunks - 1);
+  const Launch vis = Launch::make(static_cast<uint32_t>(nchunks), grid.x);
+  return launch(stream_rw_kernel<T>, grid, dim3(kThreads), st, x, nb, q, s, smap, vis) == hipSuccess
              ? NVFP4_OK
              : NVFP4_ERR_HIP;
 }
@@ -373,6 +426,8 @@ nvfp4_status rotquant_swizzled(const T* x, int64_t rows, int64_t cols, int rotat
                                uint8_t* s, float* g, float* amax, hipStream_t st) {
   const int64_t sbytes = swizzled_bytes(rows, cols);
   if (sbytes < 0) return NVFP4_ERR_SHAPE;
+  // 128 rows of input (a row tile) are addressed with 32-bit offsets
+  if (cols >= (int64_t{1} << 31) / (128 * static_cast<int64_t>(sizeof(T)))) return NVFP4_ERR_SHAPE;
   int64_t nb = 0;
   nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, false, sbytes);
   if (r != NVFP4_OK) return r;
@@ -413,8 +468,11 @@ nvfp4_status quant_from_amax(const T* x, int64_t rows, int64_t cols, int rotate,
   int64_t nb = 0;
   nvfp4_status r = validate_quant(x, rows, cols, rotate, q, s, g, amax, &nb, true);
   if (r != NVFP4_OK) return r;
-  return enqueue_quant(x, nb, rotate, reinterpret_cast<const uint32_t*>(amax), 0, nullptr, q, s, g,
-                       st);
+  // the amax word is only read (the kernel writes through amax_src on the
+  // per-workgroup-maxima path alone)
+  return enqueue_quant<T, kGiven>(x, nb, rotate,
+                                  const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(amax)), 0, nullptr,
+                                  q, s, g, st);
 }
 
 

@@ -109,21 +109,40 @@ __device__ __forceinline__ void quad_stages_4_8(float z[4], uint32_t lane) {
 
 // ---------------------------------------------------------------- division
 
-// RN(1/6) as a binary32.
+// RN(1/6) and RN(1/24) = RN(1/6) / 4 as binary32.
 constexpr float kRecip6 = 0.16666667163372040f;
+constexpr float kRecip24 = 0.041666667908430100f;
 
 // Correctly rounded y / d given r = RN(1/d): Markstein's correction step,
 // q0 = RN(y r), e = y - d q0 (exact), q1 = RN(q0 + e r).  q0 adds +0 so that a
 // zero y gives +0 whatever the signs of y, d and r.  Enumerated on the CPU
 // (tests/helpers/fastdiv.c): equal to IEEE division at every input near an
-// E2M1 or E4M3 decision boundary for every divisor significand, for the
-// divide by 6 at every input >= 2^-124, and code-for-code on random inputs
-// over the whole range the fast path admits (divisors in [2^-60, 2^16), values
-// multiples of 2^-133 as every bf16 input and every butterfly sum of them is).
+// E4M3 decision boundary for every divisor significand, and for the divides
+// by 6 and by 24 at every input >= 2^-124 and >= 2^-122.
 __device__ __forceinline__ float div_corrected(float y, float d, float r) {
   const float q0 = __builtin_fmaf(y, r, 0.0f);
   const float e = __builtin_fmaf(-q0, d, y);
   return __builtin_fmaf(e, r, q0);
+}
+
+// Two-word reciprocal of D: rh = RN(1/D) and rl = RN((1 - rh D) / D), the
+// residual 1 - rh D being exact as one fused multiply-add.  rh + rl is 1/D
+// within 2^-47 relative.
+__device__ __forceinline__ float2 recip2(float d) {
+  const float rh = 1.0f / d;
+  return make_float2(rh, __builtin_fmaf(-rh, d, 1.0f) / d);
+}
+
+// z / D from its two-word reciprocal (rh, rl): p = RN(z rl + 0),
+// q = RN(z rh + p).  q is RN(z/D (1 + eps)) with |eps| < 2^-46, so it is the
+// correctly rounded quotient or an adjacent binary32; its E2M1 code equals
+// that of the correctly rounded quotient for every input of the kernels'
+// fast path (exhaustive over the inputs near every E2M1 decision boundary,
+// for every divisor significand, tests/helpers/fastdiv.c).  A zero z gives
+// +0 (the +0 of p absorbs a -0 product).
+__device__ __forceinline__ float quot2(float z, float rh, float rl) {
+  const float p = __builtin_fmaf(z, rl, 0.0f);
+  return __builtin_fmaf(z, rh, p);
 }
 
 // ---------------------------------------------------------------- conversions
@@ -134,10 +153,15 @@ __device__ __forceinline__ float div_corrected(float y, float d, float r) {
 // in [0, 448] matches the definition (tests/test_instructions_gpu.py).  Above
 // 464 it would give NaN, hence the clamp first: min(v, 448) rounds to the
 // same byte as min(round(v), 448) (section 2, _round_e4m3; section 3).
-__device__ __forceinline__ uint32_t e4m3_byte(float v) {
+// e4m3_byte_lo leaves bits 8..31 of the result unspecified (the instruction
+// writes only the low half; the other bits are those of an unrelated
+// register), for callers that use the low byte alone.
+__device__ __forceinline__ uint32_t e4m3_byte_lo(float v) {
   const float c = __builtin_fminf(v, 448.0f);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false)) & 0xFFu;
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, static_cast<int>(__float_as_uint(v)), false));
 }
+__device__ __forceinline__ uint32_t e4m3_byte(float v) { return e4m3_byte_lo(v) & 0xFFu; }
 
 // Value of an E4M3FN byte (exact).
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
@@ -153,8 +177,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 // 0 since -0.0 < 0 is false).  Callers therefore never pass -0.0: the
 // corrected quotient returns +0 for any zero input, and the exact path adds
 // +0.0 (which turns -0.0 into +0.0 and leaves every other value unchanged).
+// The four conversions write one byte each, so the destination's initial
+// bits never reach the result; they are taken from q[0], whose register is
+// free after the first conversion (no register has to be zeroed first).
 __device__ __forceinline__ uint32_t e2m1_pack8(const float q[8]) {
-  uint32_t w = 0;
+  uint32_t w = __float_as_uint(q[0]);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);

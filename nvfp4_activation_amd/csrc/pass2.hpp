@@ -26,13 +26,17 @@ namespace {  // one translation unit (nvfp4rq.hip): internal linkage
 // blocks.  Swizzled: a super-tile of 128 rows x 16 blocks, so that one
 // workgroup writes whole 512-byte scale tiles and whole 128-byte lines of
 // codes (lines completed from several L2s are written back piecemeal).
+// Chunk counts and visit indices are 32-bit (the host keeps the chunk count
+// below 2^31), so the loop control stays in scalar registers.
 struct RowMajorScales {
   static constexpr int kSub = 1;
   static constexpr bool kStaged = false;
   int xcd_order;  // give each XCD runs of 4 consecutive chunks
   int mirror;     // a workgroup per chunk, workgroup i taking chunk nchunks - 1 - i
   __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
-  __host__ __device__ int64_t chunks(int64_t nb) const { return (nb + kThreads - 1) / kThreads; }
+  __host__ __device__ uint32_t chunks(int64_t nb) const {
+    return static_cast<uint32_t>((nb + kThreads - 1) / kThreads);
+  }
   // Workgroups go round-robin to the 8 XCDs, each with its own L2 and address
   // translation caches.  The order gives each XCD runs of 4 consecutive
   // chunks (32 KiB of bf16 input): visit index i runs on XCD i % 8 and takes
@@ -47,15 +51,9 @@ struct RowMajorScales {
   // With a workgroup per chunk the dispatcher starts workgroups in index
   // order, so mirror keeps the last chunks (the likeliest to be still cached
   // after an amax pass) first.
-  __device__ __forceinline__ int64_t order(int64_t i, int64_t nchunks) const {
+  __host__ __device__ uint32_t order(uint32_t i, uint32_t nchunks) const {
     if (mirror) return nchunks - 1 - i;
-    return xcd_order ? (i & ~int64_t{31}) | ((i & 7) << 2) | ((i >> 3) & 3) : i;
-  }
-  __device__ __forceinline__ bool locate(int64_t chunk, int, uint32_t tid, int64_t nb, int64_t* b,
-                                         int64_t* si) const {
-    *b = chunk * kThreads + tid;
-    *si = *b;
-    return *b < nb;
+    return xcd_order ? (i & ~31u) | ((i & 7u) << 2) | ((i >> 3) & 3u) : i;
   }
 };
 struct SwizzledScales {
@@ -71,9 +69,9 @@ struct SwizzledScales {
     int64_t rt;
     uint32_t cw;
   };
-  __device__ __forceinline__ Tile split(int64_t chunk) const {
-    const int64_t rt = chunk / cs;
-    return Tile{rt, static_cast<uint32_t>(chunk - rt * cs)};
+  __host__ __device__ Tile split(uint32_t chunk) const {
+    const uint32_t rt = chunk / cs;
+    return Tile{rt, chunk - rt * cs};
   }
   __device__ __forceinline__ static int64_t place(uint32_t r, uint32_t c, uint32_t ctiles) {
     const uint64_t tile = static_cast<uint64_t>(r >> 7) * ctiles + (c >> 2);
@@ -84,7 +82,9 @@ struct SwizzledScales {
     const uint32_t r = bb / cb;
     return place(r, bb - r * cb, ctiles);
   }
-  __host__ __device__ int64_t chunks(int64_t) const { return ((rows + 127) / 128) * cs; }
+  __host__ __device__ uint32_t chunks(int64_t) const {
+    return static_cast<uint32_t>(((rows + 127) / 128) * cs);
+  }
   // runs16: visit index i (on XCD i % 8) takes chunk (i & ~127) | ((i & 7)
   // << 4) | ((i >> 3) & 15), so each XCD reads 16 consecutive column windows
   // of a row tile (8 KiB of every bf16 row) instead of one.  Step at
@@ -93,9 +93,9 @@ struct SwizzledScales {
   // 23.6 us.  Used when a row tile holds a multiple of 16 windows (at
   // 32768 x 14336, 56 windows, runs of 16 cost 2.7%) and the chunk count is a
   // multiple of 128.
-  __device__ __forceinline__ int64_t order(int64_t i, int64_t nchunks) const {
+  __host__ __device__ uint32_t order(uint32_t i, uint32_t nchunks) const {
     if (mirror) return nchunks - 1 - i;
-    return runs16 ? (i & ~int64_t{127}) | ((i & 7) << 4) | ((i >> 3) & 15) : i;
+    return runs16 ? (i & ~127u) | ((i & 7u) << 4) | ((i >> 3) & 15u) : i;
   }
   __device__ __forceinline__ bool locate(Tile t, int sub, uint32_t tid, int64_t* b, int64_t* si) const {
     const uint32_t r = static_cast<uint32_t>(t.rt * 128 + sub * 16 + (tid >> 4));
@@ -106,40 +106,91 @@ struct SwizzledScales {
     return true;
   }
   // The chunk's tiles (rt, 4 cw .. 4 cw + 3) are consecutive in memory.
-  __device__ __forceinline__ void chunk_tiles(Tile t, int64_t* first_byte, int* ntiles) const {
+  __host__ __device__ void chunk_tiles(Tile t, int64_t* first_byte, int* ntiles) const {
     const int64_t ct0 = static_cast<int64_t>(t.cw) * 4;
     *first_byte = (t.rt * ctiles + ct0) * 512;
     *ntiles = static_cast<int>(ctiles - ct0 < 4 ? ctiles - ct0 : 4);
   }
 };
 
-// When pass 1 leaves its per-workgroup maxima at the head of q_out (chunk 0,
-// with the arrival counters in chunk 1), every pass-2 workgroup reads them in
-// its prologue and then counts itself in.  One workgroup alone, the one that
-// draws chunk 0, waits for all of them to have done so and then writes both
-// head chunks; nobody else waits, so the count always completes, and no
-// counter is written over while another workgroup still reads it.  Chunks run
-// last-first, so that wait comes at the end of its workgroup.  It is bounded:
-// past spin_limit sleeps the workgroup goes on and marks the call failed with
-// a NaN global scale.
+// Number of chunks workgroup wg of a grid of g visits: visit indices wg,
+// wg + g, wg + 2g, ... below nchunks.
+__host__ __device__ inline uint32_t chunks_of(uint32_t wg, uint32_t g, uint32_t nchunks) {
+  return wg < nchunks ? (nchunks - wg + g - 1) / g : 0u;
+}
+
+// Launch shape of the quantize pass, computed once on the host and passed as
+// one argument, so that a workgroup's first addresses and its fast-path
+// decision need nothing read later: the chunk count, the grid size, and the
+// number of chunks each workgroup visits from nchunks = base * grid + extra
+// (a division on the device would be emulated on the vector unit and delay
+// each workgroup's first loads): base + 1 for wg < extra, base for the
+// others.  allow_fast: 0 forces the exact divisions (tests).
+struct Launch {
+  uint32_t nchunks, base, extra, grid;
+  int allow_fast;
+  __host__ __device__ uint32_t of(uint32_t wg) const { return base + (wg < extra ? 1u : 0u); }
+  __host__ static Launch make(uint32_t nchunks, uint32_t grid, int allow_fast = 1) {
+    return Launch{nchunks, nchunks / grid, nchunks % grid, grid, allow_fast};
+  }
+};
+
+// Where the quantize pass takes the global amax from (a template argument,
+// so that each workgroup's first loads depend on nothing read at run time):
+//   kHead   pass 1's per-workgroup maxima at the head of an output (below);
+//   kWord   one amax word written by pass 1 on the same tensor;
+//   kGiven  one amax word kept from elsewhere (the given-scale call): block
+//           quotients may then leave the range the fast quotient is proven
+//           on, and such blocks divide exactly.
+enum AmaxMode { kHead = 0, kWord = 1, kGiven = 2 };
+
+// ---------------------------------------------------------------- head of the output
+
+// When pass 1 leaves its per-workgroup maxima at the head of an output (the
+// codes for the row-major layout, the scales for the swizzled one: the first
+// 2 KiB, chunk 0's bytes, with the arrival counters in the next 2 KiB, chunk
+// 1's), every pass-2 workgroup reads them in its prologue and then counts
+// itself in.  Workgroup 0 alone writes both head chunks: the visit order is
+// changed so that its last two visits are chunk 1 (visit G, G the grid size)
+// and then chunk 0 (visit 0); the workgroup that the plain order gives chunk
+// 1 takes chunk order(G) instead, so every workgroup keeps its number of
+// chunks (the host launches at most nchunks - 1 workgroups, so that
+// workgroup 0 has both visits).  Before storing chunk 1 it waits for every
+// workgroup to have counted itself in; nobody else waits, so the count
+// always completes, and no counter is written over while another workgroup
+// still reads it.  Chunks run last-first, so that wait comes after all of
+// workgroup 0's other chunks.  It is bounded in time: past `ticks` of the
+// device's constant-rate wall clock the workgroup goes on and marks the call
+// failed with a NaN global scale and a NaN amax (the codes and scales are
+// then unspecified).
+template <typename SMAP>
+__host__ __device__ inline uint32_t head_order(const SMAP& smap, uint32_t i, uint32_t nchunks, uint32_t grid,
+                                               bool head) {
+  if (!head) return smap.order(i, nchunks);
+  if (i == grid) return 1u;
+  const uint32_t c = smap.order(i, nchunks);
+  return c == 1u ? smap.order(grid, nchunks) : c;
+}
+
 struct HeadGuard {
-  uint32_t* counters;  // null: no maxima in q_out
+  uint32_t* counters;  // null: the amax came as one word
   uint32_t need;       // quantize workgroups
-  uint32_t spin_limit;
+  uint64_t ticks;
   float* gscale_out;
+  float* amax_out;
 };
 
 __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
   __shared__ int timed_out;
   if (threadIdx.x < 64) {  // wave 0: one counter per lane (lanes past kCounters add 0)
-    uint32_t spins = 0;
+    const uint64_t t0 = static_cast<uint64_t>(wall_clock64());
     int late = 0;
     // Each poll reads a counter with a fetch-and-add of zero: an atomic,
     // performed where the increments are performed, so no copy of the line
-    // in another cache can answer it.  Relaxed ordering: acquire/release at agent scope would write back or
-    // invalidate the L2 of every XCD involved on each poll.  Nothing written
-    // by other workgroups is read after the wait; the waiter's stores follow
-    // the loop.
+    // in another cache can answer it.  Relaxed ordering: acquire/release at
+    // agent scope would write back or invalidate the L2 of every XCD
+    // involved on each poll.  Nothing written by other workgroups is read
+    // after the wait; the waiter's stores follow the loop.
     // The compiler turns an add of a literal 0 back into a load, so the zero
     // is made opaque to it (an empty asm statement that only claims to
     // change the register).
@@ -153,7 +204,7 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
       if (c >= h.need) break;
-      if (++spins > h.spin_limit) {
+      if (static_cast<uint64_t>(wall_clock64()) - t0 > h.ticks) {
         late = 1;
         break;
       }
@@ -162,53 +213,87 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
     if (threadIdx.x == 0) timed_out = late;
   }
   __syncthreads();
-  if (timed_out && threadIdx.x == 0) *h.gscale_out = __uint_as_float(0x7FC00000u);
+  if (timed_out && threadIdx.x == 0) {
+    *h.gscale_out = __uint_as_float(0x7FC00000u);
+    if (h.amax_out) *h.amax_out = __uint_as_float(0x7FC00000u);
+  }
 }
 
-// A lane's first block, loaded (as raw bits) before the kernel's prologue so
-// that the load latency overlaps the amax reduction and the table set-up.
+// ---------------------------------------------------------------- raw buffer access
+
+// Row-major chunks are read and written through raw buffer resources whose
+// base is the chunk's first byte and whose size is its valid part: the
+// address arithmetic stays in scalar registers, and in the tensor's last,
+// partial chunk the lanes past its end load zeros and have their stores
+// dropped by the hardware's range check, so no lane needs a bounds test.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
+constexpr int kNontemporal = 2;           // cache-policy bit of a non-temporal access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kBufferWord3);
+}
+
+// A lane's block as raw bits.
 template <typename T>
-struct FirstBlock;
+struct Block;
 template <>
-struct FirstBlock<uint16_t> {
-  uint4 a, b;
-  __device__ __forceinline__ void load(const uint16_t* x, int64_t blk) {
-    const uint4* p = reinterpret_cast<const uint4*>(x + blk * 16);
-    a = p[0];
-    b = p[1];
+struct Block<uint16_t> {
+  u32x4 a, b;
+  __device__ __forceinline__ void load(const uint16_t* x, uint32_t chunk, uint32_t valid, uint32_t tid) {
+    const auto r = chunk_rsrc(x + static_cast<int64_t>(chunk) * (kThreads * 16), valid * 32u);
+    a = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 32u, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 32u + 16u, 0, 0);
+  }
+  // block `blk` of a buffer resource that starts at a block boundary
+  __device__ __forceinline__ void load_at(__amdgpu_buffer_rsrc_t r, uint32_t blk) {
+    a = __builtin_amdgcn_raw_buffer_load_b128(r, blk * 32u, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(r, blk * 32u + 16u, 0, 0);
   }
   __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
-    widen8(a, lo);
-    widen8(b, hi);
+    widen8(make_uint4(a.x, a.y, a.z, a.w), lo);
+    widen8(make_uint4(b.x, b.y, b.z, b.w), hi);
   }
 };
 template <>
-struct FirstBlock<float> {
-  float4 a, b, c, d;
-  __device__ __forceinline__ void load(const float* x, int64_t blk) {
-    const float4* p = reinterpret_cast<const float4*>(x + blk * 16);
-    a = p[0];
-    b = p[1];
-    c = p[2];
-    d = p[3];
+struct Block<float> {
+  u32x4 a, b, c, d;
+  __device__ __forceinline__ void load(const float* x, uint32_t chunk, uint32_t valid, uint32_t tid) {
+    const auto r = chunk_rsrc(x + static_cast<int64_t>(chunk) * (kThreads * 16), valid * 64u);
+    a = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 64u, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 64u + 16u, 0, 0);
+    c = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 64u + 32u, 0, 0);
+    d = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 64u + 48u, 0, 0);
+  }
+  __device__ __forceinline__ void load_at(__amdgpu_buffer_rsrc_t r, uint32_t blk) {
+    a = __builtin_amdgcn_raw_buffer_load_b128(r, blk * 64u, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(r, blk * 64u + 16u, 0, 0);
+    c = __builtin_amdgcn_raw_buffer_load_b128(r, blk * 64u + 32u, 0, 0);
+    d = __builtin_amdgcn_raw_buffer_load_b128(r, blk * 64u + 48u, 0, 0);
   }
   __device__ __forceinline__ void unpack(float lo[8], float hi[8]) const {
-    lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
-    lo[4] = b.x; lo[5] = b.y; lo[6] = b.z; lo[7] = b.w;
-    hi[0] = c.x; hi[1] = c.y; hi[2] = c.z; hi[3] = c.w;
-    hi[4] = d.x; hi[5] = d.y; hi[6] = d.z; hi[7] = d.w;
+    const u32x4 v[4] = {a, b, c, d};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float* o = k < 2 ? lo + 4 * k : hi + 4 * (k - 2);
+      o[0] = __uint_as_float(v[k].x);
+      o[1] = __uint_as_float(v[k].y);
+      o[2] = __uint_as_float(v[k].z);
+      o[3] = __uint_as_float(v[k].w);
+    }
   }
 };
 
-template <typename T, typename SMAP>
-__device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, SMAP smap,
-                                           FirstBlock<T>* f) {
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
-  int64_t b, si;
-  if (mine > 0 && smap.locate(smap.order((mine - 1) * gridDim.x + blockIdx.x, nchunks), 0,
-                              threadIdx.x, nb, &b, &si))
-    f->load(x, b);
+// Codes (8 bytes per lane, stored non-temporally: nothing reads them back
+// here, and in the last-level cache they would only displace input that this
+// pass re-reads: 16384 x 8192 step 1.6 us faster, 32768 x 14336 4.8 us) and
+// the scale byte (the low byte of sb) of chunk `chunk`.
+__device__ __forceinline__ void store_chunk_block(uint8_t* q, uint8_t* s, uint32_t chunk, uint32_t valid,
+                                                  uint32_t tid, u32x2 w, uint32_t sb) {
+  const auto rq = chunk_rsrc(q + static_cast<int64_t>(chunk) * (kThreads * 8), valid * 8u);
+  __builtin_amdgcn_raw_buffer_store_b64(w, rq, tid * 8u, 0, kNontemporal);
+  const auto rs = chunk_rsrc(s + static_cast<int64_t>(chunk) * kThreads, valid);
+  __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(sb), rs, tid, 0, 0);
 }
 
 // The lane's block of the workgroup's second chunk (bf16, row-major), loaded
@@ -220,13 +305,16 @@ __device__ __forceinline__ void load_first(const T* __restrict__ x, int64_t nb, 
 // block back under the same condition.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
-__device__ __forceinline__ bool prefetches_second(int64_t mine) { return mine >= 3; }
+__device__ __forceinline__ bool prefetches_second(uint32_t mine) { return mine >= 3; }
 __device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, int64_t nb,
-                                                RowMajorScales smap, uint4* pre) {
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+                                                RowMajorScales smap, Launch vis, bool head, uint4* pre) {
+  const uint32_t nchunks = vis.nchunks;
+  const uint32_t mine = vis.of(blockIdx.x);
   if (!prefetches_second(mine)) return;
-  const int64_t b = smap.order((mine - 2) * gridDim.x + blockIdx.x, nchunks) * kThreads + threadIdx.x;
+  const int64_t b =
+      static_cast<int64_t>(head_order(smap, (mine - 2) * vis.grid + blockIdx.x, nchunks, vis.grid, head)) *
+          kThreads +
+      threadIdx.x;
   if (b >= nb) return;
   const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
   // pre holds the blocks' first halves at [0, kThreads) and their second
@@ -244,13 +332,14 @@ __device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, 
 // no registers to spare for the row-major pass's early first-block load):
 // 16384 x 8192 swizzled step 101.3 -> 100.65 us, three A/B pairs.
 __device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x, int64_t nb,
-                                                  SwizzledScales smap, uint4* pre) {
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+                                                  SwizzledScales smap, Launch vis, bool head, uint4* pre) {
+  const uint32_t nchunks = vis.nchunks;
+  const uint32_t mine = vis.of(blockIdx.x);
   if (mine < 1) return;
   int64_t b, si;
-  if (!smap.locate(smap.split(smap.order((mine - 1) * gridDim.x + blockIdx.x, nchunks)), 0, threadIdx.x, &b,
-                   &si))
+  if (!smap.locate(
+          smap.split(head_order(smap, (mine - 1) * vis.grid + blockIdx.x, nchunks, vis.grid, head)), 0,
+          threadIdx.x, &b, &si))
     return;
   const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
   const int w = threadIdx.x >> 6;
@@ -258,6 +347,8 @@ __device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x
   __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(pre + kThreads + w * 64), 16, 0,
                                    0);
 }
+
+// ---------------------------------------------------------------- one block
 
 // One block of pass 2, in one lane: rotation (in place on lo, hi), the block
 // scale byte and the two words of E2M1 codes.  Every step is the definition
@@ -267,11 +358,16 @@ __device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x
 //   v     = (a_b / 6) / g,  s = E4M3(min(v, 448))
 //   d     = float(s) * g, or 1 when that is 0
 //   code  = E2M1(y / d),  y = 0.25 z
-// FAST (bf16 in the guarded range): y / d = z / (4d) exactly (the scalings by
-// 4 are exact there), the divisions are corrected reciprocal products and the
-// per-scale (4d, 1/(4d)) pairs come from a 128-entry table in LDS.
-// Otherwise every division is a true binary32 division.
-template <bool ROTATE, bool FAST>
+// FAST (bf16 in the guarded range): the scalings by 4 are exact there, so
+// a_b / 6 = max |z| / 24 and y / d = z / (4d); the block value's divisions are
+// corrected reciprocal products, and each element's code comes from the
+// two-word reciprocal of 4d (a 128-entry LDS table indexed by the scale
+// byte).  Otherwise every division is a true binary32 division.  GUARD: the
+// global scale may come from another tensor's amax, so a block's quotients
+// can exceed the range the two-word quotient is proven on; such a block
+// divides exactly.  sb_out: the scale byte in bits 0..7, other bits
+// unspecified.
+template <bool ROTATE, bool FAST, bool GUARD>
 __device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, float rg,
                                              const float2* __restrict__ tab, uint32_t* sb_out,
                                              u32x2* w_out) {
@@ -286,23 +382,23 @@ __device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, 
     az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
   uint32_t sb;
   if (FAST) {
-    const float ab = ROTATE ? 0.25f * az : az;
-    const float a6 = div_corrected(ab, 6.0f, kRecip6);
+    const float a6 = ROTATE ? div_corrected(az, 24.0f, kRecip24) : div_corrected(az, 6.0f, kRecip6);
     // A quotient too large for binary32 makes the product NaN; fminf keeps
     // 448, the right byte for any block value that large.
-    sb = e4m3_byte(div_corrected(a6, g, rg));
-    const float2 t = tab[sb];
-    if (az <= kQuotientLimit * t.x) {
+    sb = e4m3_byte_lo(div_corrected(a6, g, rg));
+    const float2 t = tab[sb & 0xFFu];
+    if (!GUARD || az * t.x <= kQuotientLimit) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        lo[i] = div_corrected(lo[i], t.x, t.y);
-        hi[i] = div_corrected(hi[i], t.x, t.y);
+        lo[i] = quot2(lo[i], t.x, t.y);
+        hi[i] = quot2(hi[i], t.x, t.y);
       }
     } else {
       // Only with a global scale from elsewhere (the amax of an earlier
       // step) can a block's quotients approach the binary32 range; divide
-      // exactly (y = z / 4 and d = 4d / 4 are exact here).
-      const float d = ROTATE ? 0.25f * t.x : t.x;
+      // exactly (y = z / 4 is exact here).
+      const float sf = e4m3_value(sb & 0xFFu) * g;
+      const float d = sf == 0.0f ? 1.0f : sf;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         lo[i] = (ROTATE ? 0.25f * lo[i] : lo[i]) / d + 0.0f;
@@ -331,126 +427,121 @@ __device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, 
   *w_out = u32x2{e2m1_pack8(lo), e2m1_pack8(hi)};
 }
 
+// ---------------------------------------------------------------- chunk loops
+
 // Pass 2 over row-major chunks (256 consecutive blocks, a block per lane).
-// Workgroup w handles the chunks w, w + G, w + 2G, ... (G = grid size), last
-// chunk first: the chunks pass 1 read last are the likeliest to still be in
-// the last-level cache.  The first chunk's blocks were loaded before the
-// prologue, so its iteration is peeled off.
-template <typename T, bool ROTATE, bool FAST, bool PRE>
+// Workgroup w handles the chunks of visits w, w + G, w + 2G, ... (G = grid
+// size), last visit first: the chunks pass 1 read last are the likeliest to
+// still be in the last-level cache.  The first chunk's blocks were loaded
+// before the prologue, so its iteration is peeled off.
+template <typename T, bool ROTATE, bool FAST, bool GUARD, bool PRE>
 __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t nb, float g,
-                                                const float2* __restrict__ tab,
-                                                uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                RowMajorScales smap, const HeadGuard& head,
-                                                const FirstBlock<T>& first,
+                                                const float2* __restrict__ tab, uint8_t* q, uint8_t* s,
+                                                RowMajorScales smap, Launch vis, const HeadGuard& head,
+                                                const Block<T>& first, const Block<T>& second,
                                                 const uint4* pre) {
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const uint32_t nchunks = vis.nchunks;
+  const uint32_t nfull = static_cast<uint32_t>(nb / kThreads);
+  const uint32_t tail = static_cast<uint32_t>(nb % kThreads);
+  const uint32_t grid = vis.grid, wg = blockIdx.x, tid = threadIdx.x;
+  const uint32_t mine = vis.of(wg);
   const float rg = FAST ? 1.0f / g : 0.0f;
-  auto finish = [&](int64_t chunk, float lo[8], float hi[8]) {
+  auto valid = [&](uint32_t chunk) -> uint32_t { return chunk < nfull ? kThreads : tail; };
+  const bool hd = head.counters != nullptr;
+  auto finish = [&](uint32_t chunk, float lo[8], float hi[8]) {
     uint32_t sb;
     u32x2 w;
-    encode_block<ROTATE, FAST>(lo, hi, g, rg, tab, &sb, &w);
-    // Codes are stored non-temporally: nothing reads them back here, and in
-    // the last-level cache they would only displace input that this pass
-    // re-reads (16384 x 8192: 1.6 us off the step; 32768 x 14336: 4.8 us).
-    u32x2* qc = reinterpret_cast<u32x2*>(q) + chunk * kThreads;
-    __builtin_nontemporal_store(w, qc + threadIdx.x);
-    (s + chunk * kThreads)[threadIdx.x] = static_cast<uint8_t>(sb);
+    encode_block<ROTATE, FAST, GUARD>(lo, hi, g, rg, tab, &sb, &w);
+    // chunk 1 holds the arrival counters: its writer (workgroup 0, see
+    // head_order) waits for the full count first; chunk 0 comes after it.
+    // Uniform across the workgroup (wait_for_head synchronizes it).
+    if (hd && chunk == 1) wait_for_head(head);
+    store_chunk_block(q, s, chunk, valid(chunk), tid, w, sb);
   };
-  // With pass 1's maxima in q_out (head.counters set), chunk 0 holds them and
-  // chunk 1 the arrival counters: the workgroup that visits chunk 0 waits
-  // until every workgroup has counted itself in, writes chunk 0 and then
-  // chunk 1; the visitor of chunk 1 skips it.  Both chunks are whole there
-  // (the host takes that path from 512 blocks).  head_ok is uniform across
-  // the workgroup (wait_for_head synchronizes it).
-  auto head_ok = [&](int64_t chunk) -> bool {  // false: skip the chunk
-    if (!head.counters || chunk > 1) return true;
-    if (chunk == 1) return false;
-    wait_for_head(head);
-    return true;
-  };
-  auto head_tail = [&](int64_t chunk) {
-    if (head.counters && chunk == 0 && kThreads + threadIdx.x < nb) {
-      float lo[8], hi[8];
-      load_block(x + kThreads * 16, threadIdx.x, lo, hi);
-      finish(1, lo, hi);
-    }
-  };
-  if (mine <= 0) return;
+  auto visit = [&](int32_t it) { return head_order(smap, static_cast<uint32_t>(it) * grid + wg, nchunks, grid, hd); };
+  if (mine == 0) return;
   {
-    const int64_t chunk = smap.order((mine - 1) * gridDim.x + blockIdx.x, nchunks);
-    if (head_ok(chunk)) {
-      if (chunk * kThreads + threadIdx.x < nb) {
-        float lo[8], hi[8];
-        first.unpack(lo, hi);
-        finish(chunk, lo, hi);
-      }
-      head_tail(chunk);
-    }
+    float lo[8], hi[8];
+    first.unpack(lo, hi);
+    finish(visit(static_cast<int32_t>(mine) - 1), lo, hi);
   }
-  int64_t it = mine - 2;
+  int32_t it = static_cast<int32_t>(mine) - 2;  // mine < 2^31
   if (PRE && prefetches_second(mine)) {  // the second chunk, from LDS (see prefetch_second)
-    const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
-    if (head_ok(chunk)) {
-      if (chunk * kThreads + threadIdx.x < nb) {
-        float lo[8], hi[8];
-        widen8(pre[threadIdx.x], lo);
-        widen8(pre[kThreads + threadIdx.x], hi);
-        finish(chunk, lo, hi);
-      }
-      head_tail(chunk);
-    }
+    float lo[8], hi[8];
+    widen8(pre[tid], lo);
+    widen8(pre[kThreads + tid], hi);
+    finish(visit(it), lo, hi);
+    --it;
+  } else if (mine == 2) {  // the second (last) chunk, preloaded into registers
+    float lo[8], hi[8];
+    second.unpack(lo, hi);
+    finish(visit(it), lo, hi);
     --it;
   }
   for (; it >= 0; --it) {
-    const int64_t chunk = smap.order(it * gridDim.x + blockIdx.x, nchunks);
-    if (!head_ok(chunk)) continue;
-    if (chunk * kThreads + threadIdx.x < nb) {
-      float lo[8], hi[8];
-      load_block(x + chunk * kThreads * 16, threadIdx.x, lo, hi);
-      finish(chunk, lo, hi);
-    }
-    head_tail(chunk);
+    const uint32_t chunk = visit(it);
+    Block<T> blk;
+    blk.load(x, chunk, valid(chunk), tid);
+    float lo[8], hi[8];
+    blk.unpack(lo, hi);
+    finish(chunk, lo, hi);
   }
 }
 
 // Pass 2 over swizzled chunks (see SwizzledScales), in the same order; the
-// chunk's scale tiles are assembled in LDS and stored whole.
+// chunk's scale tiles are assembled in LDS and stored whole.  With pass 1's
+// maxima in the scale buffer (head.counters set), chunk 0's tiles hold them
+// and chunk 1's tiles the arrival counters, and the same rule as for the
+// row-major layout applies (head_order): workgroup 0 computes chunk 1, waits,
+// stores its tiles, and then does chunk 0.  Codes never overlap the head and
+// are stored as they are computed.
 template <typename T, bool ROTATE, bool FAST, typename SMAP, bool PRE>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
-                                             const float2* __restrict__ tab,
-                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                             SMAP smap, const HeadGuard& head, const uint4* pre) {
-  // The swizzled layout never has pass 1's maxima in q_out: the host gives
-  // it the amax as one word (its head would span a whole row of tiles).
-  (void)head;
-  const int64_t nchunks = smap.chunks(nb);
-  const int64_t mine = (nchunks - blockIdx.x + gridDim.x - 1) / gridDim.x;
+                                             const float2* __restrict__ tab, uint8_t* q, uint8_t* s,
+                                             SMAP smap, Launch vis, const HeadGuard& head, const uint4* pre) {
+  const uint32_t nchunks = vis.nchunks;
+  const uint32_t mine = vis.of(blockIdx.x);
   const float rg = FAST ? 1.0f / g : 0.0f;
+  const bool hd = head.counters != nullptr;
   __shared__ uint32_t stage[512];  // 4 scale tiles
-  for (int64_t it = mine - 1; it >= 0; --it) {
-    const auto tile = smap.split(smap.order(it * gridDim.x + blockIdx.x, nchunks));
+  for (int32_t it = static_cast<int32_t>(mine) - 1; it >= 0; --it) {
+    const uint32_t chunk =
+        head_order(smap, static_cast<uint32_t>(it) * vis.grid + blockIdx.x, nchunks, vis.grid, hd);
+    const auto tile = smap.split(chunk);
+    // The chunk's row tile through raw buffer resources (block offsets within
+    // the tile fit in 32 bits: the host keeps 128 rows of input below 2^31
+    // bytes); the prefetched first blocks come from LDS.
+    const int64_t row0 = tile.rt * 128;
+    const uint32_t rows_here = static_cast<uint32_t>(smap.rows - row0 < 128 ? smap.rows - row0 : 128);
+    const int64_t tile_blocks = row0 * smap.cb;
+    const auto rx = chunk_rsrc(x + tile_blocks * 16, rows_here * smap.cb * 16u * static_cast<uint32_t>(sizeof(T)));
+    const auto rq = chunk_rsrc(q + tile_blocks * 8, rows_here * smap.cb * 8u);
     for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
     __syncthreads();
+    const uint32_t c = tile.cw * 16 + (threadIdx.x & 15u);
 #pragma unroll 1
     for (int sub = 0; sub < SMAP::kSub; ++sub) {
-      int64_t b, si;
-      if (!smap.locate(tile, sub, threadIdx.x, &b, &si)) continue;
+      const uint32_t r = static_cast<uint32_t>(sub) * 16u + (threadIdx.x >> 4);  // row within the tile
+      if (r >= rows_here || c >= smap.cb) continue;
+      const uint32_t blk = r * smap.cb + c;
       float lo[8], hi[8];
-      if (PRE && it == mine - 1 && sub == 0) {
+      if (PRE && it == static_cast<int32_t>(mine) - 1 && sub == 0) {
         widen8(pre[threadIdx.x], lo);
         widen8(pre[kThreads + threadIdx.x], hi);
       } else {
-        load_block(x, b, lo, hi);
+        Block<T> bl;
+        bl.load_at(rx, blk);
+        bl.unpack(lo, hi);
       }
       uint32_t sb;
       u32x2 w;
-      encode_block<ROTATE, FAST>(lo, hi, g, rg, tab, &sb, &w);
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(q + b * 8));
-      reinterpret_cast<uint8_t*>(stage)[si] = static_cast<uint8_t>(sb);
+      encode_block<ROTATE, FAST, false>(lo, hi, g, rg, tab, &sb, &w);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rq, blk * 8u, 0, kNontemporal);
+      reinterpret_cast<uint8_t*>(stage)[SwizzledScales::place(r, c & 15u, 4)] = static_cast<uint8_t>(sb);
     }
-    // whole tiles, padding zeros included, in one coalesced store
     __syncthreads();
+    if (hd && chunk == 1) wait_for_head(head);
+    // whole tiles, padding zeros included, in one coalesced store
     int64_t first;
     int ntiles;
     smap.chunk_tiles(tile, &first, &ntiles);
@@ -461,30 +552,50 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
   }
 }
 
-// amax_src: the amax word (npartials == 0) or pass 1's per-workgroup maxima
-// at the head of q (npartials of them, then the arrival counters; amax_out
-// receives their maximum).
+// ---------------------------------------------------------------- kernel
+
+// amax_src: the amax word (kWord, kGiven) or pass 1's per-workgroup maxima
+// at the head of q (row-major) or s (swizzled): npartials of them, then the
+// arrival counters; amax_out receives their maximum.  q and s carry no
+// __restrict__: the head is read and counted on through amax_src and later
+// overwritten through q or s.
 // Eight workgroups per CU (the grid size assumes it): at most 64 VGPRs.
-template <typename T, bool ROTATE, typename SMAP>
+template <typename T, bool ROTATE, typename SMAP, AmaxMode MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(
-    const T* __restrict__ x, int64_t nb, const uint32_t* amax_src, int npartials,
-    float* __restrict__ amax_out, uint32_t spin_limit, int allow_fast, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ s, float* __restrict__ gscale_out, SMAP smap) {
+    const T* __restrict__ x, int64_t nb, uint32_t* amax_src, int npartials, float* amax_out,
+    uint64_t head_ticks, uint8_t* q, uint8_t* s, float* gscale_out, SMAP smap, Launch vis) {
+  constexpr bool hd = MODE == kHead;
+  constexpr bool kGuard = MODE == kGiven;
   __shared__ float2 tab[128];
   __shared__ uint32_t red[kThreads / 64];
-  FirstBlock<T> first;
-  if constexpr (!SMAP::kStaged) load_first(x, nb, smap, &first);  // staged: no registers to spare
+  Block<T> first, second;
+  if constexpr (!SMAP::kStaged) {  // staged: no registers to spare
+    const uint32_t mine = vis.of(blockIdx.x);
+    const uint32_t nfull = static_cast<uint32_t>(nb / kThreads);
+    if (mine > 0) {
+      const uint32_t c = head_order(smap, (mine - 1) * vis.grid + blockIdx.x, vis.nchunks, vis.grid, hd);
+      first.load(x, c, c < nfull ? kThreads : static_cast<uint32_t>(nb % kThreads), threadIdx.x);
+    }
+    // A workgroup with exactly two chunks loads the second one up front as
+    // well (8 more registers; from three chunks on the second goes through
+    // LDS, see prefetch_second): 4096 x 4096 pass 2 8.18 -> 8.10 us, step
+    // 19.38 -> 19.13 us (three interleaved runs).
+    if (mine == 2) {
+      const uint32_t c = head_order(smap, blockIdx.x, vis.nchunks, vis.grid, hd);
+      second.load(x, c, c < nfull ? kThreads : static_cast<uint32_t>(nb % kThreads), threadIdx.x);
+    }
+  }
   constexpr bool kPre = sizeof(T) == 2;
   __shared__ uint4 pre[kPre ? 2 : 1][kPre ? kThreads : 1];  // one element where unused
   if constexpr (kPre) {
     if constexpr (SMAP::kStaged)
-      prefetch_first_sw(x, nb, smap, &pre[0][0]);
+      prefetch_first_sw(x, nb, smap, vis, hd, &pre[0][0]);
     else
-      prefetch_second(x, nb, smap, &pre[0][0]);
+      prefetch_second(x, nb, smap, vis, hd, &pre[0][0]);
   }
-  HeadGuard head{nullptr, 0, spin_limit, gscale_out};
+  HeadGuard head{nullptr, 0, head_ticks, gscale_out, amax_out};
   uint32_t abits;
-  if (npartials == 0) {
+  if constexpr (!hd) {
     abits = *amax_src;
   } else {
     uint32_t m = 0u;
@@ -495,7 +606,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     abits = red[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) abits = umax(abits, red[i]);
-    uint32_t* counters = const_cast<uint32_t*>(amax_src) + kCounterBase;
+    uint32_t* counters = amax_src + kCounterBase;
     // every thread's read of the partials is complete (their values met at
     // the barrier) before the workgroup counts itself in; a relaxed increment
     // needs no cache write-back
@@ -503,30 +614,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (blockIdx.x == 0 && threadIdx.x == 0) *amax_out = __uint_as_float(abits);
-    head = HeadGuard{counters, gridDim.x, spin_limit, gscale_out};
+    head = HeadGuard{counters, vis.grid, head_ticks, gscale_out, amax_out};
   }
   const float g = global_scale(__uint_as_float(abits));
   if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
   if constexpr (sizeof(T) == 2) {
     // uniform across the grid: every workgroup reads the same amax
-    if (allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
+    if (vis.allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
       if (threadIdx.x < 128) {
         const float sf = e4m3_value(threadIdx.x) * g;
-        const float d = (ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf);
-        tab[threadIdx.x] = make_float2(d, 1.0f / d);
+        tab[threadIdx.x] = recip2((ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf));
       }
       __syncthreads();
       if constexpr (SMAP::kStaged)
-        quant_blocks<T, ROTATE, true, SMAP, kPre>(x, nb, g, tab, q, s, smap, head, &pre[0][0]);
+        quant_blocks<T, ROTATE, true, SMAP, kPre>(x, nb, g, tab, q, s, smap, vis, head, &pre[0][0]);
       else
-        quant_blocks_rm<T, ROTATE, true, kPre>(x, nb, g, tab, q, s, smap, head, first, &pre[0][0]);
+        quant_blocks_rm<T, ROTATE, true, kGuard, kPre>(x, nb, g, tab, q, s, smap, vis, head, first, second,
+                                                      &pre[0][0]);
       return;
     }
   }
   if constexpr (SMAP::kStaged)
-    quant_blocks<T, ROTATE, false, SMAP, kPre>(x, nb, g, tab, q, s, smap, head, &pre[0][0]);
+    quant_blocks<T, ROTATE, false, SMAP, kPre>(x, nb, g, tab, q, s, smap, vis, head, &pre[0][0]);
   else
-    quant_blocks_rm<T, ROTATE, false, kPre>(x, nb, g, tab, q, s, smap, head, first, &pre[0][0]);
+    quant_blocks_rm<T, ROTATE, false, kGuard, kPre>(x, nb, g, tab, q, s, smap, vis, head, first, second,
+                                                   &pre[0][0]);
 }
 
 }  // namespace

@@ -2,7 +2,8 @@
 and check every kernel's register use.  The quantize pass is pinned to 8 waves
 per SIMD (64 VGPRs); past that the compiler spills to scratch memory, which
 costs a large part of the pass's bandwidth without changing any result, so
-only this test notices it."""
+only this test notices it.  Scalar registers the compiler parks in lanes of
+a vector register (no memory traffic) are allowed; scratch memory is not."""
 from __future__ import annotations
 
 import os
@@ -37,12 +38,15 @@ def kernels(tmp_path_factory):
 
 def test_no_kernel_spills(kernels):
     for name, r in kernels.items():
-        assert r["vgpr_spill_count"] == 0 and r["sgpr_spill_count"] == 0, (name, r)
+        assert r["vgpr_spill_count"] == 0, (name, r)
         assert r["private_segment_fixed_size"] == 0, (name, r)
+        assert r["sgpr_spill_count"] <= 8, (name, r)
 
 
 def test_quantize_pass_fits_eight_waves(kernels):
     quant = {n: r for n, r in kernels.items() if "rotquant_kernel" in n}
-    assert len(quant) == 8
+    # bf16/fp32 x rotate on/off x (row-major: head, word, given scale;
+    # swizzled: head, word)
+    assert len(quant) == 20
     for name, r in quant.items():
         assert r["vgpr_count"] <= 64, (name, r)

@@ -490,18 +490,28 @@ def test_partials_path_equals_zeroed_word_path(nv, monkeypatch, dtype):
         compare(f"partials {dtype} grids {a_wgs}/{q_wgs}", x, True, got)
 
 
-def test_head_wait_with_tiny_spin_limit(nv, monkeypatch):
-    """A spin limit of one sleep: the wait either completes in time (output
-    equal to the oracle) or gives up and marks the call with a NaN scale;
-    either way every workgroup exits."""
-    monkeypatch.setenv("NVFP4RQ_SPIN_LIMIT", "1")
+def test_head_wait_with_tiny_time_limit(nv, monkeypatch):
+    """A head-wait limit of one microsecond: the wait either completes in time
+    (output equal to the oracle) or gives up and marks the call with a NaN
+    global scale and a NaN amax; either way every workgroup exits.  Row-major
+    codes and swizzled scales both carry the head."""
+    monkeypatch.setenv("NVFP4RQ_HEAD_TIMEOUT_US", "1")
     x = mixed_input(1024, 4096, "bf16", seed=12)
     xd = to_dev(x)
+    ref = oracle.quantize(x, True)
     for _ in range(3):
-        q, s, g, a = nv.rotquant(xd)
-        torch.cuda.synchronize()
-        if not np.isnan(g.cpu().numpy()[0]):
-            compare("tiny spin limit", x, True, (q, s, g, a))
+        for call in (nv.rotquant, nv.rotquant_swizzled):
+            q, s, g, a = call(xd)
+            torch.cuda.synchronize()
+            gv, av = g.cpu().numpy()[0], a.cpu().numpy()[0]
+            if np.isnan(gv):
+                assert np.isnan(av), "a failed wait marks the amax too"
+                continue
+            if call is nv.rotquant:
+                compare("tiny head-wait limit", x, True, (q, s, g, a), ref)
+            else:
+                assert np.array_equal(s.cpu().numpy(), oracle.swizzle_scales(ref[1]))
+                assert np.array_equal(q.cpu().numpy(), ref[0])
 
 
 def test_timed_entry_point(nv):

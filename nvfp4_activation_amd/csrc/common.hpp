@@ -104,6 +104,18 @@ __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v
 
 __global__ void zero_word_kernel(uint32_t* __restrict__ w) { *w = 0u; }
 
+// Raw buffer resources: a base address and a size in bytes; the address
+// arithmetic stays in scalar registers, and lanes whose offset falls past the
+// size load zeros and have their stores dropped by the hardware's range
+// check.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
+constexpr int kNontemporal = 2;           // cache-policy bit of a non-temporal access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kBufferWord3);
+}
+
 // Non-temporal loads and stores: data that no later pass will find in (or
 // should take from) the caches.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -136,13 +136,19 @@ int amax_grid(int64_t nb, bool bf16) {
   return clamp_grid(want, (nb + per_wg - 1) / per_wg);
 }
 
-// Pass 2 when it first reduces pass 1's per-workgroup maxima: 8 workgroups
-// per compute unit, one 256-block chunk per iteration (with the amax as one
-// word, enqueue_quant launches a workgroup per chunk instead).
-int quant_grid(int64_t nb) {
+// Pass 2 when it first reduces pass 1's per-workgroup maxima: one 256-block
+// chunk per iteration, 8 workgroups per compute unit (the occupancy the
+// kernel's 64 registers allow), or 12 for bf16 inputs of at least 96 chunks
+// per compute unit, which then run in one and a half waves of workgroups
+// (16384 x 8192, step: 93.8-93.9 us with 12 per CU against 97.9-98.0 with
+// 8, 95.0 with 10 and 95.2 with 14; at 4096 x 4096, 16 chunks per CU, 12 per
+// CU cost 1.3 us; fp32 65536 x 1024 within noise from 8 to 14).  With the
+// amax as one word, enqueue_quant launches a workgroup per chunk instead.
+int quant_grid(int64_t nb, bool bf16) {
   int64_t want = env_int("NVFP4RQ_QUANT_WGS");
-  if (!want) want = 8LL * device_cus();
-  return clamp_grid(want, (nb + kThreads - 1) / kThreads);
+  const int64_t cus = device_cus(), nchunks = (nb + kThreads - 1) / kThreads;
+  if (!want) want = (bf16 && nchunks >= 96 * cus ? 12 : 8) * cus;
+  return clamp_grid(want, nchunks);
 }
 
 // Rotation alone: one workgroup per kThreads * kQuarters quarters (16384 x
@@ -283,7 +289,7 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_sr
                            SMAP smap = SMAP{}) {
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
   const int64_t nchunks = smap.chunks(nb);
-  dim3 grid(quant_grid(nchunks * kThreads));
+  dim3 grid(quant_grid(nchunks * kThreads, sizeof(T) == 2));
   if constexpr (MODE != kHead) {
     // Amax given as a word: the workgroup prologue is a single load, and a
     // workgroup per chunk beats 8 persistent ones per CU (16384 x 8192 bf16,
@@ -394,7 +400,7 @@ nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q
   uint32_t* word = reinterpret_cast<uint32_t*>(q);
   RowMajorScales smap{};
   const int64_t nchunks = smap.chunks(nb);
-  dim3 grid(quant_grid(nchunks * kThreads));
+  dim3 grid(quant_grid(nchunks * kThreads, sizeof(T) == 2));
   if (zeroed_word_path(g1, nb, large)) {
     if (launch(zero_word_kernel, dim3(1), dim3(1), st, word) != hipSuccess) return NVFP4_ERR_HIP;
     if (launch_stream_read(x, nb, word, 0, st) != hipSuccess) return NVFP4_ERR_HIP;

@@ -226,13 +226,6 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
 // address arithmetic stays in scalar registers, and in the tensor's last,
 // partial chunk the lanes past its end load zeros and have their stores
 // dropped by the hardware's range check, so no lane needs a bounds test.
-constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
-constexpr int kNontemporal = 2;           // cache-policy bit of a non-temporal access
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           kBufferWord3);
-}
 
 // A lane's block as raw bits.
 template <typename T>
@@ -367,10 +360,11 @@ __device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x
 // can exceed the range the two-word quotient is proven on; such a block
 // divides exactly.  sb_out: the scale byte in bits 0..7, other bits
 // unspecified.
-template <bool ROTATE, bool FAST, bool GUARD>
-__device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, float rg,
-                                             const float2* __restrict__ tab, uint32_t* sb_out,
-                                             u32x2* w_out) {
+// The first half: z = S16 x in place (x itself when not rotating) and the
+// block's largest |z|.  Needs no scale, so a workgroup's first block goes
+// through it while the prologue derives the scales.
+template <bool ROTATE>
+__device__ __forceinline__ float rotate_block(float lo[8], float hi[8]) {
   if (ROTATE) {
     stages_1_2_4(lo);
     stages_1_2_4(hi);
@@ -380,6 +374,14 @@ __device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, 
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     az = __builtin_fmaxf(__builtin_fmaxf(az, __builtin_fabsf(lo[i])), __builtin_fabsf(hi[i]));
+  return az;
+}
+
+// The second half, from rotate_block's output.
+template <bool ROTATE, bool FAST, bool GUARD>
+__device__ __forceinline__ void quantize_block(float lo[8], float hi[8], float az, float g, float rg,
+                                               const float2* __restrict__ tab, uint32_t* sb_out,
+                                               u32x2* w_out) {
   uint32_t sb;
   if (FAST) {
     const float a6 = ROTATE ? div_corrected(az, 24.0f, kRecip24) : div_corrected(az, 6.0f, kRecip6);
@@ -427,6 +429,14 @@ __device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, 
   *w_out = u32x2{e2m1_pack8(lo), e2m1_pack8(hi)};
 }
 
+template <bool ROTATE, bool FAST, bool GUARD>
+__device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, float rg,
+                                             const float2* __restrict__ tab, uint32_t* sb_out,
+                                             u32x2* w_out) {
+  const float az = rotate_block<ROTATE>(lo, hi);
+  quantize_block<ROTATE, FAST, GUARD>(lo, hi, az, g, rg, tab, sb_out, w_out);
+}
+
 // ---------------------------------------------------------------- chunk loops
 
 // Pass 2 over row-major chunks (256 consecutive blocks, a block per lane).
@@ -435,46 +445,43 @@ __device__ __forceinline__ void encode_block(float lo[8], float hi[8], float g, 
 // still be in the last-level cache.  The first chunk's blocks were loaded
 // before the prologue, so its iteration is peeled off.
 template <typename T, bool ROTATE, bool FAST, bool GUARD, bool PRE>
-__device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t nb, float g,
+__device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t nb, float g, float rg,
                                                 const float2* __restrict__ tab, uint8_t* q, uint8_t* s,
                                                 RowMajorScales smap, Launch vis, const HeadGuard& head,
-                                                const Block<T>& first, const Block<T>& second,
-                                                const uint4* pre) {
+                                                float flo[8], float fhi[8], float faz, const uint4* pre) {
   const uint32_t nchunks = vis.nchunks;
   const uint32_t nfull = static_cast<uint32_t>(nb / kThreads);
   const uint32_t tail = static_cast<uint32_t>(nb % kThreads);
   const uint32_t grid = vis.grid, wg = blockIdx.x, tid = threadIdx.x;
   const uint32_t mine = vis.of(wg);
-  const float rg = FAST ? 1.0f / g : 0.0f;
   auto valid = [&](uint32_t chunk) -> uint32_t { return chunk < nfull ? kThreads : tail; };
   const bool hd = head.counters != nullptr;
-  auto finish = [&](uint32_t chunk, float lo[8], float hi[8]) {
-    uint32_t sb;
-    u32x2 w;
-    encode_block<ROTATE, FAST, GUARD>(lo, hi, g, rg, tab, &sb, &w);
+  auto store = [&](uint32_t chunk, u32x2 w, uint32_t sb) {
     // chunk 1 holds the arrival counters: its writer (workgroup 0, see
     // head_order) waits for the full count first; chunk 0 comes after it.
     // Uniform across the workgroup (wait_for_head synchronizes it).
     if (hd && chunk == 1) wait_for_head(head);
     store_chunk_block(q, s, chunk, valid(chunk), tid, w, sb);
   };
+  auto finish = [&](uint32_t chunk, float lo[8], float hi[8]) {
+    uint32_t sb;
+    u32x2 w;
+    encode_block<ROTATE, FAST, GUARD>(lo, hi, g, rg, tab, &sb, &w);
+    store(chunk, w, sb);
+  };
   auto visit = [&](int32_t it) { return head_order(smap, static_cast<uint32_t>(it) * grid + wg, nchunks, grid, hd); };
   if (mine == 0) return;
-  {
-    float lo[8], hi[8];
-    first.unpack(lo, hi);
-    finish(visit(static_cast<int32_t>(mine) - 1), lo, hi);
+  {  // the first chunk's block, rotated before the prologue's barrier
+    uint32_t sb;
+    u32x2 w;
+    quantize_block<ROTATE, FAST, GUARD>(flo, fhi, faz, g, rg, tab, &sb, &w);
+    store(visit(static_cast<int32_t>(mine) - 1), w, sb);
   }
   int32_t it = static_cast<int32_t>(mine) - 2;  // mine < 2^31
   if (PRE && prefetches_second(mine)) {  // the second chunk, from LDS (see prefetch_second)
     float lo[8], hi[8];
     widen8(pre[tid], lo);
     widen8(pre[kThreads + tid], hi);
-    finish(visit(it), lo, hi);
-    --it;
-  } else if (mine == 2) {  // the second (last) chunk, preloaded into registers
-    float lo[8], hi[8];
-    second.unpack(lo, hi);
     finish(visit(it), lo, hi);
     --it;
   }
@@ -496,12 +503,11 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
 // stores its tiles, and then does chunk 0.  Codes never overlap the head and
 // are stored as they are computed.
 template <typename T, bool ROTATE, bool FAST, typename SMAP, bool PRE>
-__device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g,
+__device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g, float rg,
                                              const float2* __restrict__ tab, uint8_t* q, uint8_t* s,
                                              SMAP smap, Launch vis, const HeadGuard& head, const uint4* pre) {
   const uint32_t nchunks = vis.nchunks;
   const uint32_t mine = vis.of(blockIdx.x);
-  const float rg = FAST ? 1.0f / g : 0.0f;
   const bool hd = head.counters != nullptr;
   __shared__ uint32_t stage[512];  // 4 scale tiles
   for (int32_t it = static_cast<int32_t>(mine) - 1; it >= 0; --it) {
@@ -567,22 +573,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   constexpr bool hd = MODE == kHead;
   constexpr bool kGuard = MODE == kGiven;
   __shared__ float2 tab[128];
-  __shared__ uint32_t red[kThreads / 64];
-  Block<T> first, second;
+  Block<T> first;
   if constexpr (!SMAP::kStaged) {  // staged: no registers to spare
     const uint32_t mine = vis.of(blockIdx.x);
     const uint32_t nfull = static_cast<uint32_t>(nb / kThreads);
     if (mine > 0) {
       const uint32_t c = head_order(smap, (mine - 1) * vis.grid + blockIdx.x, vis.nchunks, vis.grid, hd);
       first.load(x, c, c < nfull ? kThreads : static_cast<uint32_t>(nb % kThreads), threadIdx.x);
-    }
-    // A workgroup with exactly two chunks loads the second one up front as
-    // well (8 more registers; from three chunks on the second goes through
-    // LDS, see prefetch_second): 4096 x 4096 pass 2 8.18 -> 8.10 us, step
-    // 19.38 -> 19.13 us (three interleaved runs).
-    if (mine == 2) {
-      const uint32_t c = head_order(smap, blockIdx.x, vis.nchunks, vis.grid, hd);
-      second.load(x, c, c < nfull ? kThreads : static_cast<uint32_t>(nb % kThreads), threadIdx.x);
     }
   }
   constexpr bool kPre = sizeof(T) == 2;
@@ -593,51 +590,88 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     else
       prefetch_second(x, nb, smap, vis, hd, &pre[0][0]);
   }
-  HeadGuard head{nullptr, 0, head_ticks, gscale_out, amax_out};
-  uint32_t abits;
-  if constexpr (!hd) {
-    abits = *amax_src;
-  } else {
-    uint32_t m = 0u;
-    for (int i = threadIdx.x; i < npartials; i += kThreads) m = umax(m, amax_src[i]);
-    m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    abits = red[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) abits = umax(abits, red[i]);
-    uint32_t* counters = amax_src + kCounterBase;
-    // every thread's read of the partials is complete (their values met at
-    // the barrier) before the workgroup counts itself in; a relaxed increment
-    // needs no cache write-back
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *amax_out = __uint_as_float(abits);
-    head = HeadGuard{counters, vis.grid, head_ticks, gscale_out, amax_out};
+  // Prologue.  Wave 0 alone derives the scalars: the global amax (reducing
+  // pass 1's maxima, then counting the workgroup in, or reading the word),
+  // g = (A / 6) / 448, 1/g and, on the fast path, the 128 two-word
+  // reciprocals; meanwhile every wave rotates its first block, which needs
+  // no scale.  One barrier then hands the scalars to all waves.
+  __shared__ uint32_t sh_abits;
+  __shared__ float sh_g, sh_rg;
+  uint32_t* counters = hd ? amax_src + kCounterBase : nullptr;
+  if (threadIdx.x < 64) {
+    uint32_t abits;
+    if constexpr (hd) {
+      // at most kMaxPartials words, in the head's first 2 KiB: two 16-byte
+      // loads per lane, words past npartials (other bytes of the output)
+      // masked out
+      const u32x4* p4 = reinterpret_cast<const u32x4*>(amax_src);
+      const u32x4 v0 = p4[threadIdx.x], v1 = p4[64 + threadIdx.x];
+      uint32_t m = 0u;
+      const int w0 = 4 * static_cast<int>(threadIdx.x), w1 = 256 + w0;
+      m = umax(m, w0 + 0 < npartials ? v0.x : 0u);
+      m = umax(m, w0 + 1 < npartials ? v0.y : 0u);
+      m = umax(m, w0 + 2 < npartials ? v0.z : 0u);
+      m = umax(m, w0 + 3 < npartials ? v0.w : 0u);
+      m = umax(m, w1 + 0 < npartials ? v1.x : 0u);
+      m = umax(m, w1 + 1 < npartials ? v1.y : 0u);
+      m = umax(m, w1 + 2 < npartials ? v1.z : 0u);
+      m = umax(m, w1 + 3 < npartials ? v1.w : 0u);
+      abits = wave_max_u32(m);
+      // this workgroup's reads of the maxima are complete (their values met
+      // in the reduction) before it counts itself in; a relaxed increment
+      // needs no cache write-back
+      if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (blockIdx.x == 0) *amax_out = __uint_as_float(abits);
+      }
+    } else {
+      abits = *amax_src;
+    }
+    const float g = global_scale(__uint_as_float(abits));
+    float rg = 0.0f;
+    if (sizeof(T) == 2 && vis.allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
+      rg = 1.0f / g;
+      for (uint32_t k = threadIdx.x; k < 128; k += 64) {
+        const float sf = e4m3_value(k) * g;
+        tab[k] = recip2((ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf));
+      }
+    }
+    if (threadIdx.x == 0) {
+      sh_abits = abits;
+      sh_g = g;
+      sh_rg = rg;
+      if (blockIdx.x == 0) *gscale_out = g;
+    }
   }
-  const float g = global_scale(__uint_as_float(abits));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gscale_out = g;
+  // (4096 x 4096: pass 2 8.10 -> 7.47 us, step 19.08 -> 18.39 us against
+  // every wave deriving the scalars itself, four interleaved runs; the
+  // fused pass at 16384 x 8192 issues 8.96 instead of 9.64 VALU
+  // lane-instructions per element)
+  float flo[8], fhi[8], faz = 0.0f;
+  if constexpr (!SMAP::kStaged) {
+    first.unpack(flo, fhi);
+    faz = rotate_block<ROTATE>(flo, fhi);
+  }
+  __syncthreads();
+  const uint32_t abits = sh_abits;
+  const float g = sh_g, rg = sh_rg;
+  const HeadGuard head{counters, vis.grid, head_ticks, gscale_out, amax_out};
   if constexpr (sizeof(T) == 2) {
     // uniform across the grid: every workgroup reads the same amax
     if (vis.allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
-      if (threadIdx.x < 128) {
-        const float sf = e4m3_value(threadIdx.x) * g;
-        tab[threadIdx.x] = recip2((ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf));
-      }
-      __syncthreads();
       if constexpr (SMAP::kStaged)
-        quant_blocks<T, ROTATE, true, SMAP, kPre>(x, nb, g, tab, q, s, smap, vis, head, &pre[0][0]);
+        quant_blocks<T, ROTATE, true, SMAP, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, &pre[0][0]);
       else
-        quant_blocks_rm<T, ROTATE, true, kGuard, kPre>(x, nb, g, tab, q, s, smap, vis, head, first, second,
+        quant_blocks_rm<T, ROTATE, true, kGuard, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, flo, fhi, faz,
                                                       &pre[0][0]);
       return;
     }
   }
   if constexpr (SMAP::kStaged)
-    quant_blocks<T, ROTATE, false, SMAP, kPre>(x, nb, g, tab, q, s, smap, vis, head, &pre[0][0]);
+    quant_blocks<T, ROTATE, false, SMAP, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, &pre[0][0]);
   else
-    quant_blocks_rm<T, ROTATE, false, kGuard, kPre>(x, nb, g, tab, q, s, smap, vis, head, first, second,
+    quant_blocks_rm<T, ROTATE, false, kGuard, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, flo, fhi, faz,
                                                    &pre[0][0]);
 }
 

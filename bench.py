@@ -95,9 +95,12 @@ def kernel_source_sha() -> str:
 
 
 def load_traffic(n_elem: int):
-    """HBM bytes per pass-2 launch from the committed rocprofv3 counter
-    summary, scaled by the copy-kernel calibration; None when the summary is
-    missing or was taken on a different kernel source."""
+    """Bytes moved beyond L2 per pass-2 launch from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration); None when the summary is missing or was taken on a
+    different kernel source.  Collected in rocprofv3's counter mode, which
+    runs the dispatches one at a time; the figure counts last-level-cache
+    hits as well as DRAM reads (no gfx950 counter separates the two)."""
     path = os.path.join(ROOT, "profiles", "rotquant_t3_lognormal_16384x8192_traffic.json")
     if not os.path.exists(path):
         return None
@@ -414,12 +417,24 @@ def main() -> int:
                      "achieved": round(p2_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(p2_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "traffic_collection": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, in KiB per "
+                                           "dispatch, scaled by a 256 MiB copy kernel's counts; "
+                                           "counter mode runs dispatches one at a time, and "
+                                           "FETCH_SIZE counts L2 misses served by the last-level "
+                                           "cache as well as by DRAM",
                      # VALU lane-instructions per element (SQ_INSTS_VALU x 64 / n);
                      # the quantize pass could issue 12.6 at the 8 TB/s element rate
                      "valu_per_element": valu,
                      "algorithmic_bytes_per_launch": nbytes["pass2"],
+                     "duration_us": round(p2 * 1e3, 3),
                      "duration": "mean of HIP events recorded at the kernel's own start and end "
-                                 "inside the fused call (hipExtLaunchKernel)"},
+                                 "inside the fused call (hipExtLaunchKernel), over the timed "
+                                 "steps of the second loop",
+                     "achieved_is": "algorithmic bytes over kernel time: by design pass 1 leaves "
+                                    "the last 160 MB of the input in the last-level cache for "
+                                    "pass 2 (up to 60% of its 268 MB read at 16384x8192), and "
+                                    "no gfx950 counter separates those hits from DRAM reads",
+                     "step_frac": round(gbs / HBM_PEAK_GBS, 4)},
         "calibration": {"kind": "no-arithmetic twins of both kernels: same grids, access patterns "
                                 "and bytes (nvfp4_stream_calibrate)",
                         "ms": round(calib_ms, 5),

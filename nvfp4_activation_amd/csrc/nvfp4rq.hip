@@ -32,6 +32,7 @@
 #include <cstddef>
 #include <cstdlib>
 #include <cstdint>
+#include <cstring>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -732,7 +733,12 @@ nvfp4_status nvfp4_stream_calibrate_f32(const float* x, int64_t rows, int64_t co
 }
 
 const char* nvfp4_status_string(nvfp4_status status) {
-  switch (status) {
+  // A C caller may pass any int.  Its bytes are read as an int: loading a value
+  // outside the enumerators' range through the C++ enum type is undefined.
+  static_assert(sizeof(nvfp4_status) == sizeof(int), "enum size");
+  int code = 0;
+  std::memcpy(&code, &status, sizeof code);
+  switch (code) {
     case NVFP4_OK: return "success";
     case NVFP4_ERR_NULL: return "a required pointer is NULL";
     case NVFP4_ERR_SHAPE: return "bad shape: rows and cols must be >= 0, cols a multiple of 16, size in range";

@@ -161,6 +161,27 @@ def cpu_baseline(x_np, rotate: bool, label: str) -> dict:
             "single_thread_sample": "first 1024 rows, both passes, median of 3"}
 
 
+def error_study(rows_cap: int, dev) -> int:
+    """The round-trip error study (nvfp4_activation_amd.error_study) on the
+    page's section-5 cases and on every synthetic workload (first `rows_cap`
+    rows), with the random orthogonal matrix drawn from seed 0."""
+    import numpy as np
+    import torch
+
+    import nvfp4_activation_amd.error_study as es
+    import synth
+
+    r = torch.from_numpy(synth.random_orthogonal16(0)).to(dev)
+    cases = es.section5_cases()
+    for name, (rows, _, _, _) in synth.WORKLOADS.items():
+        w = synth.make(name, rotate=True, rows=min(rows, rows_cap))
+        t = (torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16) if w.x.dtype == np.uint16
+             else torch.from_numpy(w.x))
+        cases[f"{name} ({t.shape[0]} rows)"] = (t, None)
+    print(es.table(es.study(cases, r)), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +192,12 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true", help="also time graph replay (context)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="synthetic workload (synth.WORKLOADS); the default is the headline one")
+    ap.add_argument("--error-study", action="store_true",
+                    help="print the plain / Hadamard / random-orthogonal round-trip error table "
+                         "(NVFP4 and MXFP4) for the page's section-5 cases and the synthetic "
+                         "workloads instead of timing")
+    ap.add_argument("--study-rows", type=int, default=4096,
+                    help="row cap for the synthetic workloads in --error-study")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
@@ -189,6 +216,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.error_study:
+        return error_study(args.study_rows, dev)
 
     if args.workload not in synth.WORKLOADS:
         print(f"unknown workload {args.workload}; one of {sorted(synth.WORKLOADS)}", file=sys.stderr)

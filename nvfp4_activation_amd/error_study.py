@@ -1,56 +1,60 @@
 """Plain versus rotated round-trip error, NVFP4 and MXFP4, on the GPU path.
 
-The study of section 5 of the page "A Fused Hadamard + NVFP4 Quantization
-Kernel in Triton" (does the 16-point rotation lower the relative L2 error
-||dequant(quant(x)) - x|| / ||x||?), together with its "Try this" item 2 (the
-same question under MXFP4: 32-element blocks, power-of-two scales) and item 3
-(a random orthogonal 16 x 16 matrix in place of the Hadamard: rotate by R,
-quantize and decode with the built-in rotation off, rotate back by R
-transposed).  Every rotation, encode and decode runs in the library's kernels;
-only the two norms are taken with PyTorch, in fp64, on the device.
+The question of section 5 of the page "A Fused Hadamard + NVFP4 Quantization
+Kernel in Triton": does the 16-point rotation lower the relative L2 error
+||dequant(quant(x)) - x|| / ||x||?  Asked here also under MXFP4 (the page's
+"Try this" item 2: 32-element blocks, power-of-two scales) and with a random
+orthogonal 16 x 16 matrix R in place of the Hadamard ("Try this" item 3:
+rotate by R, quantize and decode with the built-in rotation off, rotate back
+by R transposed).  Every rotation, encode and decode runs in the library's
+kernels; only the two norms are taken with PyTorch, in fp64, on the device.
 
-Cases: the page's three 256 x 64 tensors, drawn with PyTorch's CPU generator
-from seed 0 in the page's order (normal with columns 3, 17 and 40 scaled by
-20, normal, Student-t with 3 degrees of freedom), the outlier tensor scored
-on all columns and on the 61 normal ones; then the synthetic activation
-workloads (seeded generators at the repository root).
-
-    python -m nvfp4_activation_amd.error_study [--rows N]
+Inputs are arguments: a tensor (and optionally a column mask) per case, and R
+as a float32 [16, 16] device tensor.  `section5_cases()` rebuilds the page's
+four cases; `python bench.py --error-study` runs the study on them and on the
+synthetic activation workloads and prints the table.
 """
 from __future__ import annotations
-
-import argparse
-import os
-import sys
 
 import torch
 
 import nvfp4_activation_amd as nv
 
-OUTLIER_COLS = (3, 17, 40)
+# section 5: the outlier tensor has these three columns scaled by 20
+OUTLIER_COLUMNS = (3, 17, 40)
+OUTLIER_GAIN = 20.0
 
 
-def page_tensors() -> dict:
-    """The section-5 tensors, as float32 CPU tensors."""
-    torch.manual_seed(0)
-    x = torch.randn(256, 64)
-    x[:, list(OUTLIER_COLS)] *= 20.0
-    gauss = torch.randn(256, 64)
-    t3 = torch.distributions.StudentT(3.0).sample((256, 64))
-    normal = torch.ones(64, dtype=torch.bool)
-    normal[list(OUTLIER_COLS)] = False
-    return {"outlier channels: all values": (x, None),
-            "outlier channels: normal cols": (x, normal),
-            "gaussian": (gauss, None),
-            "student-t, 3 dof": (t3, None)}
+def section5_cases() -> dict:
+    """The page's section-5 cases as {key: (float32 CPU tensor, column mask or
+    None)}.  Its three 256 x 64 tensors come from PyTorch's CPU generator
+    seeded with 0, drawn in the page's order: a normal tensor (which then gets
+    the outlier columns), a second normal tensor, a Student-t sample with 3
+    degrees of freedom.  The outlier tensor is scored twice: on every column
+    and on the 61 columns without outliers."""
+    gen_state = torch.random.get_rng_state()
+    try:
+        torch.manual_seed(0)
+        draws = [torch.randn(256, 64), torch.randn(256, 64),
+                 torch.distributions.StudentT(3.0).sample((256, 64))]
+    finally:
+        torch.random.set_rng_state(gen_state)
+    outliers, gauss, t3 = draws
+    cols = list(OUTLIER_COLUMNS)
+    outliers[:, cols] *= OUTLIER_GAIN
+    plain_cols = torch.ones(outliers.shape[1], dtype=torch.bool)
+    plain_cols[cols] = False
+    return {"outlier_all": (outliers, None), "outlier_normal": (outliers, plain_cols),
+            "gaussian": (gauss, None), "student_t3": (t3, None)}
 
 
 def relative_error(x: torch.Tensor, xr: torch.Tensor, cols: torch.Tensor | None = None) -> float:
-    x, xr = x.double(), xr.double()
+    """||xr - x|| / ||x|| in fp64, over the columns `cols` selects (all when None)."""
+    a, b = x.double(), xr.double()
     if cols is not None:
-        cols = cols.to(x.device)
-        x, xr = x[:, cols], xr[:, cols]
-    return ((xr - x).norm() / x.norm()).item()
+        keep = cols.to(a.device)
+        a, b = a[:, keep], b[:, keep]
+    return (torch.linalg.vector_norm(b - a) / torch.linalg.vector_norm(a)).item()
 
 
 def nvfp4_error(x: torch.Tensor, rotate: bool, cols=None) -> float:
@@ -61,14 +65,6 @@ def nvfp4_error(x: torch.Tensor, rotate: bool, cols=None) -> float:
 def mxfp4_error(x: torch.Tensor, rotate: bool, cols=None) -> float:
     q, s = nv.mx_rotquant(x, rotate=rotate)
     return relative_error(x, nv.mx_dequant(q, s, rotate=rotate), cols)
-
-
-def orthogonal(device, seed: int = 0) -> torch.Tensor:
-    """The random orthogonal matrix (seeded Haar draw from the generators at
-    the repository root), on the device."""
-    _root_on_path()
-    import synth
-    return torch.from_numpy(synth.random_orthogonal16(seed)).to(device)
 
 
 def nvfp4_orth_error(x: torch.Tensor, r: torch.Tensor, cols=None) -> float:
@@ -83,37 +79,19 @@ def mxfp4_orth_error(x: torch.Tensor, r: torch.Tensor, cols=None) -> float:
     return relative_error(x, back, cols)
 
 
-def study_row(x: torch.Tensor, cols=None) -> dict:
-    r = orthogonal(x.device)
+def study_row(x: torch.Tensor, r: torch.Tensor, cols=None) -> dict:
+    """The six errors of one case: NVFP4 and MXFP4, each plain, with the
+    built-in Hadamard rotation and with R."""
     return {"nvfp4_plain": nvfp4_error(x, False, cols), "nvfp4_rotated": nvfp4_error(x, True, cols),
             "nvfp4_orth": nvfp4_orth_error(x, r, cols),
             "mxfp4_plain": mxfp4_error(x, False, cols), "mxfp4_rotated": mxfp4_error(x, True, cols),
             "mxfp4_orth": mxfp4_orth_error(x, r, cols)}
 
 
-def page_study(device="cuda:0") -> dict:
-    return {name: study_row(t.to(device), cols) for name, (t, cols) in page_tensors().items()}
-
-
-def _root_on_path():
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    if root not in sys.path:
-        sys.path.insert(0, root)
-
-
-def workload_study(rows_cap: int, device="cuda:0") -> dict:
-    _root_on_path()
-    import numpy as np
-    import synth
-    out = {}
-    for name, (rows, _, _, _) in synth.WORKLOADS.items():
-        w = synth.make(name, rotate=True, rows=min(rows, rows_cap))
-        if w.x.dtype == np.uint16:
-            x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(device)
-        else:
-            x = torch.from_numpy(w.x).to(device)
-        out[f"{name} ({x.shape[0]} rows)"] = study_row(x)
-    return out
+def study(cases: dict, r: torch.Tensor) -> dict:
+    """{key: study_row} for {key: (tensor, column mask or None)}; each tensor
+    is moved to R's device."""
+    return {k: study_row(t.to(r.device), r, cols) for k, (t, cols) in cases.items()}
 
 
 def table(rows: dict) -> str:
@@ -123,17 +101,3 @@ def table(rows: dict) -> str:
         f"| {k} | {v['nvfp4_plain']:.4f} | {v['nvfp4_rotated']:.4f} | {v['nvfp4_orth']:.4f} | "
         f"{v['mxfp4_plain']:.4f} | {v['mxfp4_rotated']:.4f} | {v['mxfp4_orth']:.4f} |\n"
         for k, v in rows.items())
-
-
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--rows", type=int, default=4096, help="row cap for the synthetic workloads")
-    args = ap.parse_args()
-    rows = page_study()
-    rows.update(workload_study(args.rows))
-    print(table(rows), flush=True)
-    return 0
-
-
-if __name__ == "__main__":
-    sys.exit(main())

@@ -165,7 +165,7 @@ def test_orthogonal_error_study_through_the_library(nv):
 
 def test_study_rows_carry_orthogonal_columns(nv):
     from nvfp4_activation_amd import error_study as es
-    rows = es.page_study()
+    rows = es.study(es.section5_cases(), torch.from_numpy(synth.random_orthogonal16(0)).to("cuda:0"))
     for name, row in rows.items():
         for key in ("nvfp4_orth", "mxfp4_orth"):
             assert 0.0 < row[key] < 1.0, (name, key, row[key])

@@ -82,13 +82,11 @@ def test_page_error_table_through_the_library(nv):
     columns agree with the oracle's fp64 round-trip errors."""
     from nvfp4_activation_amd import error_study as es
     expected = {r[0]: (float(r[1]), float(r[2])) for r in read_golden("error_table.txt")}
-    keys = {"outlier channels: all values": "outlier_all",
-            "outlier channels: normal cols": "outlier_normal",
-            "gaussian": "gaussian", "student-t, 3 dof": "student_t3"}
-    rows = es.page_study()
-    tensors = es.page_tensors()
+    tensors = es.section5_cases()
+    assert sorted(tensors) == sorted(expected)
+    rows = es.study(tensors, torch.from_numpy(synth.random_orthogonal16(0)).to("cuda:0"))
     for name, r in rows.items():
-        plain, rot = expected[keys[name]]
+        plain, rot = expected[name]
         assert round(r["nvfp4_plain"], 4) == plain, (name, r)
         assert round(r["nvfp4_rotated"], 4) == rot, (name, r)
         t, cols = tensors[name]

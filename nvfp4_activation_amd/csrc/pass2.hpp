@@ -292,32 +292,31 @@ __device__ __forceinline__ void store_chunk_block(uint8_t* q, uint8_t* s, uint32
 // The lane's block of the workgroup's second chunk (bf16, row-major), loaded
 // before the prologue straight into LDS (the kernel has no registers to spare
 // for it), 8 KiB per workgroup: 16384 x 8192 step 97.5 -> 95.7 us, pass 2
-// 52.6 -> 51.1 us (three A/B pairs).  Used from 3 chunks per workgroup: with
-// 2 (4096 x 4096) the prologue, whose wait for the maxima also waits for
-// these loads, made the step 0.25 us slower.  quant_blocks_rm reads the
-// block back under the same condition.
+// 52.6 -> 51.1 us (three A/B pairs).  Through a buffer resource whose size is
+// the chunk's valid part (0 when the workgroup has fewer than two chunks), so
+// the loads are issued unconditionally: with no branch between wave 0's loads
+// of the maxima and their use, the wait for them can leave these loads in
+// flight.  quant_blocks_rm reads the block back when prefetches_second.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
-__device__ __forceinline__ bool prefetches_second(uint32_t mine) { return mine >= 3; }
+__device__ __forceinline__ bool prefetches_second(uint32_t mine) { return mine >= 2; }
 __device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, int64_t nb,
                                                 RowMajorScales smap, Launch vis, bool head, uint4* pre) {
   const uint32_t nchunks = vis.nchunks;
   const uint32_t mine = vis.of(blockIdx.x);
-  if (!prefetches_second(mine)) return;
-  const int64_t b =
-      static_cast<int64_t>(head_order(smap, (mine - 2) * vis.grid + blockIdx.x, nchunks, vis.grid, head)) *
-          kThreads +
-      threadIdx.x;
-  if (b >= nb) return;
-  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
+  const bool on = prefetches_second(mine);
+  const uint32_t c = on ? head_order(smap, (mine - 2) * vis.grid + blockIdx.x, nchunks, vis.grid, head) : 0u;
+  const uint32_t nfull = static_cast<uint32_t>(nb / kThreads);
+  const uint32_t valid = !on ? 0u : c < nfull ? static_cast<uint32_t>(kThreads) : static_cast<uint32_t>(nb % kThreads);
+  const auto r = chunk_rsrc(x + static_cast<int64_t>(c) * (kThreads * 16), valid * 32u);
   // pre holds the blocks' first halves at [0, kThreads) and their second
-  // halves at [kThreads, 2 kThreads).  The destination operand is per wave:
-  // lane l's 16 bytes land at slot 64 w + l, i.e. at threadIdx.x.
-  // Address-space conversions take C-style casts.
+  // halves at [kThreads, 2 kThreads).  The destination is per wave: lane l's
+  // 16 bytes land at slot 64 w + l, i.e. at threadIdx.x.  Address-space
+  // conversions take C-style casts.
   const int w = threadIdx.x >> 6;
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(p), (lds_void_ptr)(pre + w * 64), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(pre + kThreads + w * 64), 16, 0,
-                                   0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(pre + w * 64), 16, threadIdx.x * 32u, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(pre + kThreads + w * 64), 16,
+                                           threadIdx.x * 32u + 16u, 0, 0, 0);
 }
 
 // Swizzled chunks: the lane's block of the first sub-iteration of the
@@ -326,19 +325,23 @@ __device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, 
 // 16384 x 8192 swizzled step 101.3 -> 100.65 us, three A/B pairs.
 __device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x, int64_t nb,
                                                   SwizzledScales smap, Launch vis, bool head, uint4* pre) {
+  (void)nb;
+  // Through a buffer resource over the chunk's row tile (its size 0 when the
+  // workgroup has no chunk; lanes outside the tensor get an offset past the
+  // end), so the loads are issued unconditionally, as in prefetch_second.
   const uint32_t nchunks = vis.nchunks;
   const uint32_t mine = vis.of(blockIdx.x);
-  if (mine < 1) return;
-  int64_t b, si;
-  if (!smap.locate(
-          smap.split(head_order(smap, (mine - 1) * vis.grid + blockIdx.x, nchunks, vis.grid, head)), 0,
-          threadIdx.x, &b, &si))
-    return;
-  const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
+  const auto tile =
+      smap.split(mine > 0 ? head_order(smap, (mine - 1) * vis.grid + blockIdx.x, nchunks, vis.grid, head) : 0u);
+  const int64_t row0 = tile.rt * 128;
+  const uint32_t rows_here =
+      mine == 0 ? 0u : static_cast<uint32_t>(smap.rows - row0 < 128 ? smap.rows - row0 : 128);
+  const auto r = chunk_rsrc(x + row0 * smap.cb * 16, rows_here * smap.cb * 32u);
+  const uint32_t rr = threadIdx.x >> 4, c = tile.cw * 16 + (threadIdx.x & 15u);
+  const uint32_t off = rr < rows_here && c < smap.cb ? (rr * smap.cb + c) * 32u : 0xFFFFFFE0u;
   const int w = threadIdx.x >> 6;
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(p), (lds_void_ptr)(pre + w * 64), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(p + 1), (lds_void_ptr)(pre + kThreads + w * 64), 16, 0,
-                                   0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(pre + w * 64), 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(pre + kThreads + w * 64), 16, off + 16u, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- one block
@@ -573,14 +576,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   constexpr bool hd = MODE == kHead;
   constexpr bool kGuard = MODE == kGiven;
   __shared__ float2 tab[128];
+  // pass 1's maxima (at most kMaxPartials words, in the head's first 2 KiB:
+  // two 16-byte loads per lane) are loaded before any block, by every wave
+  // although only wave 0 reduces them: with no branch between these loads and
+  // their use, wave 0's wait for them leaves the block loads and the LDS
+  // prefetch below in flight (loads complete in issue order).
+  u32x4 part0 = {0u, 0u, 0u, 0u}, part1 = {0u, 0u, 0u, 0u};
+  if constexpr (hd) {
+    const u32x4* p4 = reinterpret_cast<const u32x4*>(amax_src);
+    part0 = p4[threadIdx.x & 63u];
+    part1 = p4[64 + (threadIdx.x & 63u)];
+  }
+  // The first chunk's block, through a buffer resource of the chunk's valid
+  // size (0 when the workgroup has no chunk): unconditional, as above.
   Block<T> first;
   if constexpr (!SMAP::kStaged) {  // staged: no registers to spare
     const uint32_t mine = vis.of(blockIdx.x);
     const uint32_t nfull = static_cast<uint32_t>(nb / kThreads);
-    if (mine > 0) {
-      const uint32_t c = head_order(smap, (mine - 1) * vis.grid + blockIdx.x, vis.nchunks, vis.grid, hd);
-      first.load(x, c, c < nfull ? kThreads : static_cast<uint32_t>(nb % kThreads), threadIdx.x);
-    }
+    const uint32_t c =
+        mine > 0 ? head_order(smap, (mine - 1) * vis.grid + blockIdx.x, vis.nchunks, vis.grid, hd) : 0u;
+    const uint32_t valid =
+        mine == 0 ? 0u : c < nfull ? static_cast<uint32_t>(kThreads) : static_cast<uint32_t>(nb % kThreads);
+    first.load(x, c, valid, threadIdx.x);
   }
   constexpr bool kPre = sizeof(T) == 2;
   __shared__ uint4 pre[kPre ? 2 : 1][kPre ? kThreads : 1];  // one element where unused
@@ -601,11 +618,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   if (threadIdx.x < 64) {
     uint32_t abits;
     if constexpr (hd) {
-      // at most kMaxPartials words, in the head's first 2 KiB: two 16-byte
-      // loads per lane, words past npartials (other bytes of the output)
-      // masked out
-      const u32x4* p4 = reinterpret_cast<const u32x4*>(amax_src);
-      const u32x4 v0 = p4[threadIdx.x], v1 = p4[64 + threadIdx.x];
+      // words past npartials (other bytes of the output) masked out
+      const u32x4 v0 = part0, v1 = part1;
       uint32_t m = 0u;
       const int w0 = 4 * static_cast<int>(threadIdx.x), w1 = 256 + w0;
       m = umax(m, w0 + 0 < npartials ? v0.x : 0u);

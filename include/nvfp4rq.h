@@ -47,8 +47,8 @@
  *   - Outputs must not overlap the input or each other (NVFP4_ERR_ARG).
  *   - Calls that share an output buffer must be ordered (same stream or
  *     explicit events): the amax word can be an atomic accumulator, and the
- *     fused calls keep pass 1's partial maxima at the head of q_out (or of
- *     s_out for the swizzled layout).
+ *     fused calls keep pass 1's partial maxima at the head of q_out (of
+ *     s_out and q_out for the swizzled layout).
  *   - No C++ exception crosses this interface.
  */
 #ifndef NVFP4RQ_H
@@ -203,11 +203,11 @@ nvfp4_status nvfp4_rotquant_f32_timed(const float *x, int64_t rows, int64_t cols
  * for bf16, < 2^22 for fp32; NVFP4_ERR_SHAPE otherwise).
  * nvfp4_rotquant_swizzled(_f32): nvfp4_rotquant with s_out in this layout
  * (s_out holds nvfp4_swizzled_scale_bytes bytes, 4-byte aligned; padding bytes
- * are written as 0).  Codes, g and amax are as for nvfp4_rotquant.  When a
- * row holds at least 8 scale tiles (cols >= 464) and two column windows of
- * 16 blocks, the call keeps pass 1's per-workgroup maxima and arrival
- * counters in the first 4 KiB of s_out instead of q_out, with the same
- * failure mark; s_out is then defined only once the call has completed.
+ * are written as 0).  Codes, g and amax are as for nvfp4_rotquant.  From 16
+ * rows and cols >= 256, the call keeps pass 1's per-workgroup maxima in the
+ * first 2 KiB of s_out and its arrival counters in the first 4 bytes of code
+ * rows 0..15 of q_out, with the same failure mark; both outputs are then
+ * defined only once the call has completed.
  * nvfp4_dequant_swizzled: nvfp4_dequant reading scales in this layout.
  */
 int64_t nvfp4_swizzled_scale_bytes(int64_t rows, int64_t cols);

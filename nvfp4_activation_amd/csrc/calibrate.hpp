@@ -22,7 +22,8 @@ __device__ __forceinline__ uint32_t fold(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w
 __global__ __launch_bounds__(kThreads) void stream_read_bf16_kernel(const uint16_t* __restrict__ x,
                                                                     int64_t nb,
                                                                     uint32_t* __restrict__ out,
-                                                                    int partials, int64_t nt_end) {
+                                                                    int partials, Counters counters,
+                                                                    int64_t nt_end) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = pass1_wg() * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
@@ -48,21 +49,21 @@ __global__ __launch_bounds__(kThreads) void stream_read_bf16_kernel(const uint16
 #pragma unroll
     for (int j = 0; j < kAmaxPieces; ++j) m ^= fold(v[j]);
   }
-  workgroup_max_to(m, out, partials);
+  workgroup_max_to(m, out, partials, counters);
 }
 
 // Twin of rotamax_f32_kernel: one 64-byte block per lane per iteration.
 __global__ __launch_bounds__(kThreads) void stream_read_f32_kernel(const float* __restrict__ x,
                                                                    int64_t nb,
                                                                    uint32_t* __restrict__ out,
-                                                                   int partials) {
+                                                                   int partials, Counters counters) {
   uint32_t m = 0u;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb; b += stride) {
     const uint4* p = reinterpret_cast<const uint4*>(x + b * 16);
     m ^= fold(p[0]) ^ fold(p[1]) ^ fold(p[2]) ^ fold(p[3]);
   }
-  workgroup_max_to(m, out, partials);
+  workgroup_max_to(m, out, partials, counters);
 }
 
 // Twin of rotquant_kernel with row-major scales: the same chunk order and

@@ -33,19 +33,29 @@ constexpr int64_t kLastLevelKeep = 160LL << 20;  // bytes of input pass 1 leaves
 // over through a zeroed word instead of per-workgroup maxima, so that pass 2
 // can run a workgroup per chunk (see enqueue_both).
 constexpr int64_t kOneShotInputBytes = 512LL << 20;
-// When pass 1 leaves its per-workgroup maxima in q_out, the head of q_out
-// (the quantize pass's chunks 0 and 1, 2 KiB of codes each) holds the maxima
-// at words [0, npartials), npartials <= kMaxPartials, and the quantize pass's
-// arrival counters in chunk 1, kCounters words on separate 128-byte lines
+// When pass 1 leaves its per-workgroup maxima in the outputs (the head), they
+// sit at words [0, npartials), npartials <= kMaxPartials, and the quantize
+// pass's arrival counters are kCounters words on separate 128-byte lines
 // (thousands of increments of one word serialize, and a workgroup's loads
-// wait behind its own pending atomic).  Only the quantize workgroup that
-// writes chunk 0 reads the counters, and it writes chunk 1 as well, after
-// chunk 0: nothing overwrites a counter that is still being read.
+// wait behind its own pending atomic).  Row-major scales: both in q_out, the
+// maxima in chunk 0's 2 KiB of codes and the counters in chunk 1's, kHeadBytes
+// in all.  Swizzled scales: the maxima in chunk 0's 2 KiB of scale tiles, the
+// counters at the start of code rows 0 .. kCounters - 1, also chunk 0's.
+// Only the quantize workgroup that writes the head's chunks reads the
+// counters, and it writes those chunks last, after its wait: nothing
+// overwrites a counter that is still being read.
 constexpr int kMaxPartials = 512;
 constexpr int kCounters = 16;
-constexpr int kCounterStride = 32;                                               // words
-constexpr int64_t kCounterBase = kMaxPartials;                                   // words
+constexpr int kCounterStride = 32;                                               // words (row-major)
+constexpr int64_t kCounterBase = kMaxPartials;                                   // words (row-major)
 constexpr int64_t kHeadBytes = 4 * (kCounterBase + kCounters * kCounterStride);  // 4096
+
+// Where the arrival counters are: kCounters words, `stride` words apart.
+struct Counters {
+  uint32_t* base;
+  uint32_t stride;
+  __host__ __device__ uint32_t* at(uint32_t i) const { return base + static_cast<int64_t>(i) * stride; }
+};
 
 // ---------------------------------------------------------------- reductions
 
@@ -82,7 +92,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
 // values order like their bit patterns, so the maximum is exact and the same
 // for any reduction order (a NaN input stays visible as bits above +inf).
 __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restrict__ out,
-                                                 int partials) {
+                                                 int partials, Counters counters) {
   __shared__ uint32_t part[kThreads / 64];
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
@@ -96,8 +106,7 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restric
     else
       atomicMax(out, r);
   }
-  if (partials && blockIdx.x == 0 && threadIdx.x < kCounters)
-    out[kCounterBase + threadIdx.x * kCounterStride] = 0u;
+  if (partials && blockIdx.x == 0 && threadIdx.x < kCounters) *counters.at(threadIdx.x) = 0u;
 }
 
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }

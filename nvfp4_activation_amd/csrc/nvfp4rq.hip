@@ -238,7 +238,7 @@ int64_t bf16_nt_end(int64_t nb) {
 }
 
 hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* bits, int partials,
-                          hipStream_t st) {
+                          hipStream_t st, Counters counters = Counters{nullptr, 0u}) {
   const dim3 grid(amax_grid(nb, true));
   // The quantize pass walks the tensor last-first and finds the part pass 1
   // read last in the 256 MB last-level cache; the part before the last
@@ -248,16 +248,17 @@ hipError_t launch_rotamax(const uint16_t* x, int64_t nb, int rotate, uint32_t* b
   // 95.9 / 96.1 us; streaming less leaves pass 1 slower, streaming more
   // costs pass 2 its cache hits.  At 32768 x 14336 the rule took 12 us off.
   const int64_t nt_end = bf16_nt_end(nb);
-  return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials, nt_end)
-                : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials,
+  return rotate ? launch(rotamax_bf16_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials, counters,
+                         nt_end)
+                : launch(rotamax_bf16_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials, counters,
                          nt_end);
 }
 
 hipError_t launch_rotamax(const float* x, int64_t nb, int rotate, uint32_t* bits, int partials,
-                          hipStream_t st) {
+                          hipStream_t st, Counters counters = Counters{nullptr, 0u}) {
   const dim3 grid(amax_grid(nb, false));
-  return rotate ? launch(rotamax_f32_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials)
-                : launch(rotamax_f32_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials);
+  return rotate ? launch(rotamax_f32_kernel<true>, grid, dim3(kThreads), st, x, nb, bits, partials, counters)
+                : launch(rotamax_f32_kernel<false>, grid, dim3(kThreads), st, x, nb, bits, partials, counters);
 }
 
 template <typename T>
@@ -282,11 +283,12 @@ uint64_t head_ticks() {
 
 // Pass 2.  MODE kWord / kGiven: the amax is the word at amax_src (written by
 // pass 1 on the same tensor, or kept from elsewhere).  kHead: amax_src holds
-// npartials per-workgroup maxima and the counters (at the head of q or s) and
-// the kernel writes their maximum to amax_out.
+// npartials per-workgroup maxima (at the head of q or s), the arrival
+// counters are at `counters`, and the kernel writes the maxima's maximum to
+// amax_out.
 template <typename T, AmaxMode MODE, typename SMAP = RowMajorScales>
 nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_src, int npartials,
-                           float* amax_out, uint8_t* q, uint8_t* s, float* g, hipStream_t st,
+                           Counters counters, float* amax_out, uint8_t* q, uint8_t* s, float* g, hipStream_t st,
                            SMAP smap = SMAP{}) {
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
   const int64_t nchunks = smap.chunks(nb);
@@ -299,9 +301,9 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_sr
     grid = dim3(clamp_grid(nchunks, nchunks));
     smap.mirror = 1;
   } else {
-    // workgroup 0 visits both head chunks (head_order): the grid leaves it two
-    // visits
-    if (grid.x > nchunks - 1) grid.x = static_cast<unsigned>(nchunks - 1);
+    // row-major: workgroup 0 visits both head chunks (head_order), so the
+    // grid leaves it two visits; the swizzled head is chunk 0 alone
+    if (SMAP::kHeadSwap && grid.x > nchunks - 1) grid.x = static_cast<unsigned>(nchunks - 1);
     if constexpr (std::is_same_v<SMAP, RowMajorScales> && sizeof(T) == 2) {
       // bf16: runs of 4 consecutive chunks per XCD (see RowMajorScales::order).
       // fp32 chunks (16 KiB) do best in plain order: at 65536 x 1024 the step
@@ -313,34 +315,37 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_sr
   const uint64_t ticks = head_ticks();
   const hipError_t e =
       rotate ? launch(rotquant_kernel<T, true, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
-                      npartials, amax_out, ticks, q, s, g, smap, vis)
+                      npartials, counters, amax_out, ticks, q, s, g, smap, vis)
              : launch(rotquant_kernel<T, false, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
-                      npartials, amax_out, ticks, q, s, g, smap, vis);
+                      npartials, counters, amax_out, ticks, q, s, g, smap, vis);
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-bool zeroed_word_path(int g1, int64_t nb, bool large) {
-  return g1 > kMaxPartials || kHeadBytes > 8 * nb || large || env_int("NVFP4RQ_ZEROED_AMAX");
+bool zeroed_word_path(int g1, bool large) {
+  return g1 > kMaxPartials || large || env_int("NVFP4RQ_ZEROED_AMAX");
 }
 
-// Where pass 1 can leave its per-workgroup maxima and the arrival counters:
-// the first kHeadBytes of q_out (row-major: chunks 0 and 1 of the codes),
-// or of s_out for the swizzled layout (the scale tiles of chunks 0 and 1,
-// which are 2 KiB each and consecutive when a row of blocks spans at least
-// 8 tiles, cols >= 464 and ctiles >= 8, and there is a second column
-// window).  A swizzled chunk is 2048 blocks; below kSwizzledHeadChunks of
-// them the one-word path's grid of one workgroup per chunk is faster than
-// a head writer with two chunks to itself (128 x 1024, 4 chunks: 21.6 us
-// against 18.9 us per step).
-constexpr int64_t kSwizzledHeadChunks = 32;
-uint32_t* head_of(uint8_t* q, uint8_t*, int64_t, RowMajorScales) { return reinterpret_cast<uint32_t*>(q); }
-uint32_t* head_of(uint8_t*, uint8_t* s, int64_t nb, const SwizzledScales& sm) {
-  return sm.ctiles >= 8 && sm.cs >= 2 && sm.chunks(nb) >= kSwizzledHeadChunks ? reinterpret_cast<uint32_t*>(s)
-                                                                                : nullptr;
+// Where pass 1 can leave its per-workgroup maxima and the arrival counters
+// (partials null: nowhere).  Row-major scales: the first kHeadBytes of q_out,
+// chunks 0 and 1 of the codes (from 512 blocks up).  Swizzled scales: the
+// maxima in the first 2 KiB of s_out, chunk 0's four scale tiles, and the
+// counters at the start of code rows 0 .. 15, chunk 0's code lines, one
+// 128-byte line each (from 16 rows and 16 blocks per row up).
+struct Head {
+  uint32_t* partials;
+  Counters counters;
+};
+Head head_of(uint8_t* q, uint8_t*, int64_t nb, RowMajorScales) {
+  if (kHeadBytes > 8 * nb) return Head{nullptr, Counters{nullptr, 0u}};
+  uint32_t* w = reinterpret_cast<uint32_t*>(q);
+  return Head{w, Counters{w + kCounterBase, static_cast<uint32_t>(kCounterStride)}};
+}
+Head head_of(uint8_t* q, uint8_t* s, int64_t, const SwizzledScales& sm) {
+  if (sm.rows < kCounters || sm.cb < 16) return Head{nullptr, Counters{nullptr, 0u}};
+  return Head{reinterpret_cast<uint32_t*>(s), Counters{reinterpret_cast<uint32_t*>(q), 2 * sm.cb}};
 }
 
-// Both passes.  When the head has room (row-major: 8 nb bytes of codes
-// against kHeadBytes, from 512 blocks up; swizzled: see head_of) and pass 1
+// Both passes.  When the head has room (see head_of) and pass 1
 // has at most kMaxPartials workgroups, pass 1 leaves per-workgroup maxima
 // and cleared counters there (which one pass-2 workgroup overwrites last), so
 // no word has to be zeroed first; other tensors and wider pass-1 grids take
@@ -359,28 +364,28 @@ nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_
   // per step at 939 MB)
   const bool large = std::is_same_v<SMAP, RowMajorScales> &&
                      nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
-  uint32_t* head = head_of(q, s, nb, smap);
-  if (nb == 0 || !head || zeroed_word_path(g1, nb, large)) {
+  const Head head = head_of(q, s, nb, smap);
+  if (nb == 0 || !head.partials || zeroed_word_path(g1, large)) {
     nvfp4_status r = enqueue_rotamax(x, nb, rotate, amax, st);
     if (r != NVFP4_OK) return r;
-    return enqueue_quant<T, kWord>(x, nb, rotate, reinterpret_cast<uint32_t*>(amax), 0, amax, q, s, g, st,
-                                   smap);
+    return enqueue_quant<T, kWord>(x, nb, rotate, reinterpret_cast<uint32_t*>(amax), 0, Counters{nullptr, 0u},
+                                   amax, q, s, g, st, smap);
   }
-  if (launch_rotamax(x, nb, rotate, head, 1, st) != hipSuccess) return NVFP4_ERR_HIP;
-  return enqueue_quant<T, kHead>(x, nb, rotate, head, g1, amax, q, s, g, st, smap);
+  if (launch_rotamax(x, nb, rotate, head.partials, 1, st, head.counters) != hipSuccess) return NVFP4_ERR_HIP;
+  return enqueue_quant<T, kHead>(x, nb, rotate, head.partials, g1, head.counters, amax, q, s, g, st, smap);
 }
 
 // Measurement support (calibrate.hpp): the fused call's launch sequence for
 // row-major scales, with the twins in place of the two passes.
 hipError_t launch_stream_read(const uint16_t* x, int64_t nb, uint32_t* out, int partials,
-                              hipStream_t st) {
+                              hipStream_t st, Counters counters) {
   return launch(stream_read_bf16_kernel, dim3(amax_grid(nb, true)), dim3(kThreads), st, x, nb, out,
-                partials, bf16_nt_end(nb));
+                partials, counters, bf16_nt_end(nb));
 }
 hipError_t launch_stream_read(const float* x, int64_t nb, uint32_t* out, int partials,
-                              hipStream_t st) {
+                              hipStream_t st, Counters counters) {
   return launch(stream_read_f32_kernel, dim3(amax_grid(nb, false)), dim3(kThreads), st, x, nb, out,
-                partials);
+                partials, counters);
 }
 
 template <typename T>
@@ -398,21 +403,23 @@ nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q
   if (nb == 0) return NVFP4_OK;
   const int g1 = amax_grid_for(x, nb);
   const bool large = nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
-  uint32_t* word = reinterpret_cast<uint32_t*>(q);
   RowMajorScales smap{};
+  const Head head = head_of(q, s, nb, smap);
+  const bool word_path = !head.partials || zeroed_word_path(g1, large);
+  uint32_t* word = reinterpret_cast<uint32_t*>(q);
   const int64_t nchunks = smap.chunks(nb);
   dim3 grid(quant_grid(nchunks * kThreads, sizeof(T) == 2));
-  if (zeroed_word_path(g1, nb, large)) {
+  if (word_path) {
     if (launch(zero_word_kernel, dim3(1), dim3(1), st, word) != hipSuccess) return NVFP4_ERR_HIP;
-    if (launch_stream_read(x, nb, word, 0, st) != hipSuccess) return NVFP4_ERR_HIP;
+    if (launch_stream_read(x, nb, word, 0, st, Counters{nullptr, 0u}) != hipSuccess) return NVFP4_ERR_HIP;
     grid = dim3(clamp_grid(nchunks, nchunks));
     smap.mirror = 1;
   } else {
-    if (launch_stream_read(x, nb, word, 1, st) != hipSuccess) return NVFP4_ERR_HIP;
+    if (launch_stream_read(x, nb, word, 1, st, head.counters) != hipSuccess) return NVFP4_ERR_HIP;
     if constexpr (sizeof(T) == 2)
       smap.xcd_order = nchunks % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
   }
-  if (!zeroed_word_path(g1, nb, large) && grid.x > nchunks - 1) grid.x = static_cast<unsigned>(nchunks - 1);
+  if (!word_path && grid.x > nchunks - 1) grid.x = static_cast<unsigned>(nchunks - 1);
   const Launch vis = Launch::make(static_cast<uint32_t>(nchunks), grid.x);
   return launch(stream_rw_kernel<T>, grid, dim3(kThreads), st, x, nb, q, s, smap, vis) == hipSuccess
              ? NVFP4_OK
@@ -478,8 +485,8 @@ nvfp4_status quant_from_amax(const T* x, int64_t rows, int64_t cols, int rotate,
   // the amax word is only read (the kernel writes through amax_src on the
   // per-workgroup-maxima path alone)
   return enqueue_quant<T, kGiven>(x, nb, rotate,
-                                  const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(amax)), 0, nullptr,
-                                  q, s, g, st);
+                                  const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(amax)), 0,
+                                  Counters{nullptr, 0u}, nullptr, q, s, g, st);
 }
 
 

@@ -27,7 +27,8 @@ template <bool ROTATE>
 __global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 int64_t nb,
                                                                 uint32_t* __restrict__ amax_bits,
-                                                                int partials, int64_t nt_end) {
+                                                                int partials, Counters counters,
+                                                                int64_t nt_end) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = pass1_wg() * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void rotamax_bf16_kernel(const uint16_t* 
     }
   }
   if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
-  workgroup_max_to(m, amax_bits, partials);
+  workgroup_max_to(m, amax_bits, partials, counters);
 }
 
 // Pass 1 for fp32: one block per lane per iteration.
@@ -74,7 +75,7 @@ template <bool ROTATE>
 __global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __restrict__ x,
                                                                int64_t nb,
                                                                uint32_t* __restrict__ amax_bits,
-                                                               int partials) {
+                                                               int partials, Counters counters) {
   uint32_t m = 0u;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nb; b += stride) {
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void rotamax_f32_kernel(const float* __re
     }
   }
   if (ROTATE) m = __float_as_uint(0.25f * __uint_as_float(m));
-  workgroup_max_to(m, amax_bits, partials);
+  workgroup_max_to(m, amax_bits, partials, counters);
 }
 
 }  // namespace

@@ -31,6 +31,7 @@ namespace {  // one translation unit (nvfp4rq.hip): internal linkage
 struct RowMajorScales {
   static constexpr int kSub = 1;
   static constexpr bool kStaged = false;
+  static constexpr bool kHeadSwap = true;  // the head spans chunks 0 and 1 (see head_order)
   int xcd_order;  // give each XCD runs of 4 consecutive chunks
   int mirror;     // a workgroup per chunk, workgroup i taking chunk nchunks - 1 - i
   __device__ __forceinline__ int64_t operator()(int64_t b) const { return b; }
@@ -58,7 +59,8 @@ struct RowMajorScales {
 };
 struct SwizzledScales {
   static constexpr int kSub = 8;
-  static constexpr bool kStaged = true;  // scale tiles assembled in LDS
+  static constexpr bool kStaged = true;     // scale tiles assembled in LDS
+  static constexpr bool kHeadSwap = false;  // the head lies in chunk 0 alone
   int64_t rows;
   uint32_t cb, ctiles, cs;  // blocks per row, ceil(cb / 4), ceil(cb / 16)
   int mirror;               // as RowMajorScales::mirror
@@ -146,19 +148,22 @@ enum AmaxMode { kHead = 0, kWord = 1, kGiven = 2 };
 
 // ---------------------------------------------------------------- head of the output
 
-// When pass 1 leaves its per-workgroup maxima at the head of an output (the
-// codes for the row-major layout, the scales for the swizzled one: the first
-// 2 KiB, chunk 0's bytes, with the arrival counters in the next 2 KiB, chunk
-// 1's), every pass-2 workgroup reads them in its prologue and then counts
-// itself in.  Workgroup 0 alone writes both head chunks: the visit order is
-// changed so that its last two visits are chunk 1 (visit G, G the grid size)
-// and then chunk 0 (visit 0); the workgroup that the plain order gives chunk
-// 1 takes chunk order(G) instead, so every workgroup keeps its number of
-// chunks (the host launches at most nchunks - 1 workgroups, so that
-// workgroup 0 has both visits).  Before storing chunk 1 it waits for every
-// workgroup to have counted itself in; nobody else waits, so the count
-// always completes, and no counter is written over while another workgroup
-// still reads it.  Chunks run last-first, so that wait comes after all of
+// When pass 1 leaves its per-workgroup maxima at the head of the outputs,
+// every pass-2 workgroup reads them in its prologue and then counts itself in
+// on one of the arrival counters.  Row-major scales: the head is the first
+// 4 KiB of the codes, chunk 0's bytes (the maxima) and chunk 1's (the
+// counters).  Workgroup 0 alone writes both chunks: the visit order is changed
+// so that its last two visits are chunk 1 (visit G, G the grid size) and then
+// chunk 0 (visit 0); the workgroup that the plain order gives chunk 1 takes
+// chunk order(G) instead, so every workgroup keeps its number of chunks (the
+// host launches at most nchunks - 1 workgroups, so that workgroup 0 has both
+// visits).  Before storing chunk 1 it waits for every workgroup to have
+// counted itself in.  Swizzled scales: the maxima fill chunk 0's scale tiles
+// and the counters sit in chunk 0's code rows, so workgroup 0's last visit,
+// chunk 0 in the plain order, is the whole head and needs no swap; it waits
+// before storing any of it.  Nobody else waits, so the count always
+// completes, and no counter is written over while another workgroup still
+// reads it.  Chunks run last-first, so that wait comes after all of
 // workgroup 0's other chunks.  It is bounded in time: past `ticks` of the
 // device's constant-rate wall clock the workgroup goes on and marks the call
 // failed with a NaN global scale and a NaN amax (the codes and scales are
@@ -166,14 +171,14 @@ enum AmaxMode { kHead = 0, kWord = 1, kGiven = 2 };
 template <typename SMAP>
 __host__ __device__ inline uint32_t head_order(const SMAP& smap, uint32_t i, uint32_t nchunks, uint32_t grid,
                                                bool head) {
-  if (!head) return smap.order(i, nchunks);
+  if (!head || !SMAP::kHeadSwap) return smap.order(i, nchunks);
   if (i == grid) return 1u;
   const uint32_t c = smap.order(i, nchunks);
   return c == 1u ? smap.order(grid, nchunks) : c;
 }
 
 struct HeadGuard {
-  uint32_t* counters;  // null: the amax came as one word
+  Counters counters;   // base null: the amax came as one word
   uint32_t need;       // quantize workgroups
   uint64_t ticks;
   float* gscale_out;
@@ -198,8 +203,8 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
     __asm__ volatile("" : "+v"(zero));
     for (;;) {
       uint32_t c = threadIdx.x < kCounters
-                       ? __hip_atomic_fetch_add(h.counters + threadIdx.x * kCounterStride, zero,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       ? __hip_atomic_fetch_add(h.counters.at(threadIdx.x), zero, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
                        : 0u;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
@@ -458,7 +463,7 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
   const uint32_t grid = vis.grid, wg = blockIdx.x, tid = threadIdx.x;
   const uint32_t mine = vis.of(wg);
   auto valid = [&](uint32_t chunk) -> uint32_t { return chunk < nfull ? kThreads : tail; };
-  const bool hd = head.counters != nullptr;
+  const bool hd = head.counters.base != nullptr;
   auto store = [&](uint32_t chunk, u32x2 w, uint32_t sb) {
     // chunk 1 holds the arrival counters: its writer (workgroup 0, see
     // head_order) waits for the full count first; chunk 0 comes after it.
@@ -499,23 +504,26 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
 }
 
 // Pass 2 over swizzled chunks (see SwizzledScales), in the same order; the
-// chunk's scale tiles are assembled in LDS and stored whole.  With pass 1's
-// maxima in the scale buffer (head.counters set), chunk 0's tiles hold them
-// and chunk 1's tiles the arrival counters, and the same rule as for the
-// row-major layout applies (head_order): workgroup 0 computes chunk 1, waits,
-// stores its tiles, and then does chunk 0.  Codes never overlap the head and
-// are stored as they are computed.
+// chunk's scale tiles are assembled in LDS and stored whole, and its codes
+// are stored as they are computed.  With pass 1's maxima at the head
+// (head.counters set), chunk 0 holds the maxima in its scale tiles and the
+// arrival counters in its first code rows; workgroup 0, whose last visit it
+// is, waits before starting it.
 template <typename T, bool ROTATE, bool FAST, typename SMAP, bool PRE>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g, float rg,
                                              const float2* __restrict__ tab, uint8_t* q, uint8_t* s,
                                              SMAP smap, Launch vis, const HeadGuard& head, const uint4* pre) {
   const uint32_t nchunks = vis.nchunks;
   const uint32_t mine = vis.of(blockIdx.x);
-  const bool hd = head.counters != nullptr;
+  const bool hd = head.counters.base != nullptr;
   __shared__ uint32_t stage[512];  // 4 scale tiles
   for (int32_t it = static_cast<int32_t>(mine) - 1; it >= 0; --it) {
     const uint32_t chunk =
         head_order(smap, static_cast<uint32_t>(it) * vis.grid + blockIdx.x, nchunks, vis.grid, hd);
+    // chunk 0 is the head (its scale tiles hold the maxima, its first code
+    // rows the counters): its writer, workgroup 0, waits before any store.
+    // Uniform across the workgroup (wait_for_head synchronizes it).
+    if (hd && chunk == 0) wait_for_head(head);
     const auto tile = smap.split(chunk);
     // The chunk's row tile through raw buffer resources (block offsets within
     // the tile fit in 32 bits: the host keeps 128 rows of input below 2^31
@@ -549,7 +557,6 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
       reinterpret_cast<uint8_t*>(stage)[SwizzledScales::place(r, c & 15u, 4)] = static_cast<uint8_t>(sb);
     }
     __syncthreads();
-    if (hd && chunk == 1) wait_for_head(head);
     // whole tiles, padding zeros included, in one coalesced store
     int64_t first;
     int ntiles;
@@ -564,14 +571,14 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
 // ---------------------------------------------------------------- kernel
 
 // amax_src: the amax word (kWord, kGiven) or pass 1's per-workgroup maxima
-// at the head of q (row-major) or s (swizzled): npartials of them, then the
-// arrival counters; amax_out receives their maximum.  q and s carry no
+// at the head of q (row-major) or s (swizzled): npartials of them, with the
+// arrival counters at `counters`; amax_out receives their maximum.  q and s carry no
 // __restrict__: the head is read and counted on through amax_src and later
 // overwritten through q or s.
 // Eight workgroups per CU (the grid size assumes it): at most 64 VGPRs.
 template <typename T, bool ROTATE, typename SMAP, AmaxMode MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(
-    const T* __restrict__ x, int64_t nb, uint32_t* amax_src, int npartials, float* amax_out,
+    const T* __restrict__ x, int64_t nb, uint32_t* amax_src, int npartials, Counters counters, float* amax_out,
     uint64_t head_ticks, uint8_t* q, uint8_t* s, float* gscale_out, SMAP smap, Launch vis) {
   constexpr bool hd = MODE == kHead;
   constexpr bool kGuard = MODE == kGiven;
@@ -614,7 +621,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   // no scale.  One barrier then hands the scalars to all waves.
   __shared__ uint32_t sh_abits;
   __shared__ float sh_g, sh_rg;
-  uint32_t* counters = hd ? amax_src + kCounterBase : nullptr;
   if (threadIdx.x < 64) {
     uint32_t abits;
     if constexpr (hd) {
@@ -635,7 +641,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       // in the reduction) before it counts itself in; a relaxed increment
       // needs no cache write-back
       if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(counters + (blockIdx.x % kCounters) * kCounterStride, 1u, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(counters.at(blockIdx.x % kCounters), 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         if (blockIdx.x == 0) *amax_out = __uint_as_float(abits);
       }
@@ -670,7 +676,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   __syncthreads();
   const uint32_t abits = sh_abits;
   const float g = sh_g, rg = sh_rg;
-  const HeadGuard head{counters, vis.grid, head_ticks, gscale_out, amax_out};
+  const HeadGuard head{hd ? counters : Counters{nullptr, 0u}, vis.grid, head_ticks, gscale_out, amax_out};
   if constexpr (sizeof(T) == 2) {
     // uniform across the grid: every workgroup reads the same amax
     if (vis.allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {

@@ -3,12 +3,15 @@
 // pass2.hpp) for many chunk counts and grid sizes:
 //   - the chunk order (with the head's swap, head_order) is a permutation:
 //     every chunk is visited, and written, exactly once;
-//   - workgroup 0 visits chunk 1 second-to-last and chunk 0 last, so it
-//     writes both head chunks, after all of its other work and after its
-//     wait, and no other workgroup writes either;
+//   - row-major: workgroup 0 visits chunk 1 second-to-last and chunk 0 last,
+//     so it writes both head chunks, after all of its other work and after
+//     its wait, and no other workgroup writes either; swizzled: workgroup 0
+//     visits chunk 0, the whole head, last;
 //   - no workgroup gets more chunks than under the plain order;
-//   - the head (chunks 0 and 1) is the first 4 KiB of the output it lives in
-//     (row-major codes; swizzled scale tiles when the host allows the head);
+//   - the head is where the host puts it: row-major, the first 4 KiB of the
+//     codes (chunks 0 and 1); swizzled, the maxima in the first 2 KiB of the
+//     scales (chunk 0's four tiles) and the counters at the start of code
+//     rows 0..15 (chunk 0's code lines), each on its own 128-byte line;
 //   - the amax pass's workgroup remap is a bijection on its grid.
 // Test code: built and run by tests/test_head_protocol_cpu.py.  Runs on the
 // host only; no GPU call is made.
@@ -37,7 +40,7 @@ static int failures = 0;
 // Walks every workgroup's visits last-first, as the kernel does.
 template <typename SMAP>
 static void check_order(const char* tag, const SMAP& smap, uint32_t nchunks, uint32_t grid, bool head) {
-  if (head && grid > nchunks - 1) grid = nchunks - 1;  // as the host launches it
+  if (head && SMAP::kHeadSwap && grid > nchunks - 1) grid = nchunks - 1;  // as the host launches it
   std::vector<int> visits(nchunks, 0), writer(nchunks, -1);
   const Launch vis = Launch::make(nchunks, grid);
   for (uint32_t wg = 0; wg < grid; ++wg) {
@@ -52,13 +55,14 @@ static void check_order(const char* tag, const SMAP& smap, uint32_t nchunks, uin
       ++visits[c];
       writer[c] = static_cast<int>(wg);
       if (head && c == 0) CHECK(wg == 0 && it == 0, "%s: chunk 0 at wg %u it %d", tag, wg, it);
-      if (head && c == 1) CHECK(wg == 0 && it == 1, "%s: chunk 1 at wg %u it %d", tag, wg, it);
+      if (head && SMAP::kHeadSwap && c == 1) CHECK(wg == 0 && it == 1, "%s: chunk 1 at wg %u it %d", tag, wg, it);
     }
   }
   for (uint32_t c = 0; c < nchunks; ++c)
     CHECK(visits[c] == 1, "%s: chunk %u visited %d times (nchunks %u, grid %u)", tag, c, visits[c], nchunks,
           grid);
-  if (head) CHECK(writer[0] == 0 && writer[1] == 0, "%s: head chunks written by %d and %d", tag, writer[0], writer[1]);
+  if (head) CHECK(writer[0] == 0, "%s: chunk 0 written by %d", tag, writer[0]);
+  if (head && SMAP::kHeadSwap) CHECK(writer[1] == 0, "%s: chunk 1 written by %d", tag, writer[1]);
 }
 
 static void check_pass1_remap(int64_t grid) {
@@ -119,14 +123,30 @@ int main() {
     const uint32_t cb = static_cast<uint32_t>(cols / 16), ctiles = (cb + 3) / 4, cs = (cb + 15) / 16;
     SwizzledScales sm{rows, cb, ctiles, cs, 0, 0};
     const uint32_t nchunks = sm.chunks(rows * cb);
-    const bool head = ctiles >= 8 && cs >= 2;
+    const bool head = rows >= kCounters && cb >= 16;  // the host's rule (head_of)
     if (head) {
-      int64_t b0, b1;
-      int t0, t1;
+      // the maxima: chunk 0's tiles are the first 2 KiB of the scales
+      int64_t b0;
+      int t0;
       sm.chunk_tiles(sm.split(0), &b0, &t0);
-      sm.chunk_tiles(sm.split(1), &b1, &t1);
-      CHECK(b0 == 0 && t0 == 4 && b1 == 2048 && t1 == 4, "swizzled %lldx%lld head tiles %lld/%d %lld/%d",
-            (long long)rows, (long long)cols, (long long)b0, t0, (long long)b1, t1);
+      CHECK(b0 == 0 && t0 == 4, "swizzled %lldx%lld head tiles %lld/%d", (long long)rows, (long long)cols,
+            (long long)b0, t0);
+      CHECK(kMaxPartials * 4 <= 4 * 512, "maxima fit chunk 0's tiles");
+      // the counters: code byte r * 8 cb of row r < 16, which chunk 0 writes
+      // (row tile 0, column window 0: code bytes 0..127 of rows 0..127), each
+      // on its own 128-byte line
+      std::vector<uint32_t> codes(static_cast<size_t>(kCounters) * 2 * cb);  // rows 0..15 of the codes
+      const Counters cn{codes.data(), 2 * cb};
+      for (uint32_t i = 0; i < kCounters; ++i) {
+        const int64_t byte = 4 * (cn.at(i) - codes.data());
+        const int64_t row = byte / (8 * cb), col_byte = byte % (8 * cb);
+        CHECK(row < 128 && row < rows && col_byte < 128, "counter %u at row %lld byte %lld", i, (long long)row,
+              (long long)col_byte);
+        CHECK(sm.split(static_cast<uint32_t>(0)).rt == row / 128 && col_byte / 128 == 0,
+              "counter %u outside chunk 0", i);
+        if (i > 0) CHECK(byte / 128 != 4 * (cn.at(i - 1) - codes.data()) / 128,
+                         "counters %u and %u share a line", i - 1, i);
+      }
     }
     for (uint32_t grid : quant_grids(nchunks)) {
       for (int r16 = 0; r16 < 2; ++r16) {

@@ -1,11 +1,12 @@
 """CPU check of the quantize pass's head protocol indexing.
 
 In the fused call pass 1 leaves its per-workgroup maxima and the arrival
-counters in the first 4 KiB of an output (chunks 0 and 1), and one pass-2
-workgroup alone writes those chunks after waiting for every workgroup to have
-read the maxima.  That is only safe if the chunk order visits each chunk once,
-gives chunk 0 to workgroup 0 as its last visit, and the skip rule leaves every
-chunk written exactly once.  tests/helpers/head_protocol.hip evaluates the
+counters in the outputs (row-major: the first 4 KiB of the codes, chunks 0 and
+1; swizzled: chunk 0's scale tiles and code rows), and one pass-2 workgroup
+alone writes those chunks after waiting for every workgroup to have read the
+maxima.  That is only safe if the chunk order visits each chunk once, gives
+chunk 0 to workgroup 0 as its last visit, and the skip rule leaves every chunk
+written exactly once.  tests/helpers/head_protocol.hip evaluates the
 kernels' own index functions on the host for the chunk counts and grids the
 library and the GPU tests use, and checks the amax pass's workgroup remap is
 a bijection.

@@ -28,23 +28,31 @@ def nv():
     return nv
 
 
+@pytest.mark.parametrize("swizzled", [False, True])
 @pytest.mark.parametrize("amax_wgs", [None, 48, 24])
 @pytest.mark.parametrize("rotate", [True, False])
-def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
+def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate, swizzled):
+    """Row-major and swizzled scales (the swizzled call keeps the maxima in its
+    scale tiles and the counters in its first code rows; on this zero input the
+    codes written over the counters are zero, so a premature head write would
+    show as a NaN global scale)."""
     if amax_wgs is None:
         monkeypatch.delenv("NVFP4RQ_AMAX_WGS", raising=False)
     else:
         monkeypatch.setenv("NVFP4RQ_AMAX_WGS", str(amax_wgs))
     rows = cols = 4096
     nchunks = rows * cols // 16 // 256
-    say(f"amax coverage: {nchunks} chunks, amax_wgs={amax_wgs}, rotate={rotate}")
+    say(f"amax coverage: {nchunks} chunks, amax_wgs={amax_wgs}, rotate={rotate}, swizzled={swizzled}")
     dev = "cuda:0"
     x = torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev)
     flat = x.view(-1)
+    sbytes = nv.swizzled_scale_bytes(rows, cols) if swizzled else rows * cols // 16
     out = (torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
+           torch.empty(sbytes, dtype=torch.uint8, device=dev) if swizzled else
            torch.empty(rows, cols // 16, dtype=torch.uint8, device=dev),
            torch.empty(1, dtype=torch.float32, device=dev),
            torch.empty(1, dtype=torch.float32, device=dev))
+    call = nv.rotquant_swizzled if swizzled else nv.rotquant
     got = torch.empty(nchunks, dtype=torch.float32, device=dev)
     got_g = torch.empty(nchunks, dtype=torch.float32, device=dev)
     big = 1024.0                       # exact in bf16; rotated, every output is +-256
@@ -54,7 +62,7 @@ def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
     # device-side index views and copies only: the loop never waits for the GPU
     for c in range(nchunks):
         flat.index_fill_(0, pos[c:c + 1], big)
-        nv.rotquant(x, rotate=rotate, out=out)
+        call(x, rotate=rotate, out=out)
         got[c:c + 1].copy_(out[3])
         got_g[c:c + 1].copy_(out[2])
         flat.index_fill_(0, pos[c:c + 1], 0.0)
@@ -69,12 +77,14 @@ def test_every_chunk_reaches_the_amax(nv, monkeypatch, amax_wgs, rotate):
     assert not bad_g, f"calls with a wrong global scale: {bad_g[:20]} ({len(bad_g)} in all)"
 
 
+@pytest.mark.parametrize("swizzled", [False, True])
 @pytest.mark.parametrize("rows,cols,calls", [(16384, 8192, 400), (2048, 8192, 2000), (4096, 4096, 2000)])
-def test_repeated_calls_keep_the_global_scale(nv, monkeypatch, rows, cols, calls):
+def test_repeated_calls_keep_the_global_scale(nv, monkeypatch, rows, cols, calls, swizzled):
     """Back-to-back fused calls on one set of buffers: every call's amax and
     global scale equal the oracle's.  The quantize workgroup that writes the
-    head of q_out first waits for every workgroup to have read pass 1's maxima
-    there; a wait that ran out would leave a NaN global scale."""
+    head (of q_out, or of s_out and q_out for swizzled scales) first waits for
+    every workgroup to have read pass 1's maxima there; a wait that ran out
+    would leave a NaN global scale."""
     monkeypatch.delenv("NVFP4RQ_AMAX_WGS", raising=False)
     monkeypatch.delenv("NVFP4RQ_QUANT_WGS", raising=False)
     import oracle
@@ -83,17 +93,21 @@ def test_repeated_calls_keep_the_global_scale(nv, monkeypatch, rows, cols, calls
     x = synth.normal_bf16(rows * cols, seed=rows + cols, stream=3).reshape(rows, cols)
     oq, os_, og, oa = oracle.quantize(x, True)
     xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    sbytes = nv.swizzled_scale_bytes(rows, cols) if swizzled else rows * cols // 16
     out = (torch.empty(rows, cols // 2, dtype=torch.uint8, device="cuda:0"),
+           torch.empty(sbytes, dtype=torch.uint8, device="cuda:0") if swizzled else
            torch.empty(rows, cols // 16, dtype=torch.uint8, device="cuda:0"),
            torch.empty(1, dtype=torch.float32, device="cuda:0"),
            torch.empty(1, dtype=torch.float32, device="cuda:0"))
+    call = nv.rotquant_swizzled if swizzled else nv.rotquant
     gs = torch.empty(calls, dtype=torch.float32, device="cuda:0")
     am = torch.empty(calls, dtype=torch.float32, device="cuda:0")
     for c in range(calls):
-        nv.rotquant(xd, rotate=True, out=out)
+        call(xd, rotate=True, out=out)
         gs[c:c + 1].copy_(out[2])
         am[c:c + 1].copy_(out[3])
     torch.cuda.synchronize()
     bad = ((gs != float(np.float32(og))) | (am != float(np.float32(oa)))).nonzero().flatten().tolist()
     assert not bad, f"calls with a wrong amax or global scale: {bad[:20]} ({len(bad)} in all)"
-    assert np.array_equal(out[0].cpu().numpy(), oq) and np.array_equal(out[1].cpu().numpy(), os_)
+    want_s = oracle.swizzle_scales(os_) if swizzled else os_
+    assert np.array_equal(out[0].cpu().numpy(), oq) and np.array_equal(out[1].cpu().numpy(), want_s)

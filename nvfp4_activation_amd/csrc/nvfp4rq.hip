@@ -313,11 +313,28 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_sr
   }
   const Launch vis = Launch::make(static_cast<uint32_t>(nchunks), grid.x, allow_fast);
   const uint64_t ticks = head_ticks();
-  const hipError_t e =
-      rotate ? launch(rotquant_kernel<T, true, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
-                      npartials, counters, amax_out, ticks, q, s, g, smap, vis)
-             : launch(rotquant_kernel<T, false, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
-                      npartials, counters, amax_out, ticks, q, s, g, smap, vis);
+  hipError_t e;
+  if constexpr (std::is_same_v<SMAP, SwizzledScales>) {
+    // Swizzled chunks are 2048 blocks.  When every chunk can have a
+    // 1024-thread workgroup at once (2 per CU at 8 waves per SIMD), such
+    // workgroups take a chunk's 128 rows in 2 sub-iterations instead of 8:
+    // 128 x 1024 (4 chunks) step 15.7 -> 12.6 us, 4096 x 4096 (512) 20.8 ->
+    // 19.8 us; with more chunks than that the 256-thread grid wins (8192 x
+    // 4096, 1024 chunks: 30.7 against 34.0 us; 16384 x 4096: 53.2 against
+    // 57.4 us).
+    const int64_t forced = env_int("NVFP4RQ_SWZ_THREADS");
+    if (forced ? forced == 1024 : nchunks <= 2LL * device_cus()) {
+      e = rotate ? launch(rotquant_kernel<T, true, SMAP, MODE, 1024>, grid, dim3(1024), st, x, nb, amax_src,
+                          npartials, counters, amax_out, ticks, q, s, g, smap, vis)
+                 : launch(rotquant_kernel<T, false, SMAP, MODE, 1024>, grid, dim3(1024), st, x, nb, amax_src,
+                          npartials, counters, amax_out, ticks, q, s, g, smap, vis);
+      return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    }
+  }
+  e = rotate ? launch(rotquant_kernel<T, true, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src, npartials,
+                      counters, amax_out, ticks, q, s, g, smap, vis)
+             : launch(rotquant_kernel<T, false, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src, npartials,
+                      counters, amax_out, ticks, q, s, g, smap, vis);
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -22,14 +22,14 @@ namespace {  // one translation unit (nvfp4rq.hip): internal linkage
 // 512 (rt * ctiles + ct) + 16 j + 4 i + k.  Block indices fit in 32 bits
 // (checked on the host).
 // Each policy also fixes which blocks a pass-2 workgroup handles together
-// (a chunk): kSub groups of kThreads blocks.  Row-major: 256 consecutive
-// blocks.  Swizzled: a super-tile of 128 rows x 16 blocks, so that one
-// workgroup writes whole 512-byte scale tiles and whole 128-byte lines of
-// codes (lines completed from several L2s are written back piecemeal).
+// (a chunk).  Row-major: 256 consecutive blocks, one per lane.  Swizzled: a
+// super-tile of 128 rows x 16 blocks (sub-iterations of 16 lanes per row), so
+// that one workgroup writes whole 512-byte scale tiles and whole 128-byte
+// lines of codes (lines completed from several L2s are written back
+// piecemeal).
 // Chunk counts and visit indices are 32-bit (the host keeps the chunk count
 // below 2^31), so the loop control stays in scalar registers.
 struct RowMajorScales {
-  static constexpr int kSub = 1;
   static constexpr bool kStaged = false;
   static constexpr bool kHeadSwap = true;  // the head spans chunks 0 and 1 (see head_order)
   int xcd_order;  // give each XCD runs of 4 consecutive chunks
@@ -58,7 +58,6 @@ struct RowMajorScales {
   }
 };
 struct SwizzledScales {
-  static constexpr int kSub = 8;
   static constexpr bool kStaged = true;     // scale tiles assembled in LDS
   static constexpr bool kHeadSwap = false;  // the head lies in chunk 0 alone
   int64_t rows;
@@ -98,14 +97,6 @@ struct SwizzledScales {
   __host__ __device__ uint32_t order(uint32_t i, uint32_t nchunks) const {
     if (mirror) return nchunks - 1 - i;
     return runs16 ? (i & ~127u) | ((i & 7u) << 4) | ((i >> 3) & 15u) : i;
-  }
-  __device__ __forceinline__ bool locate(Tile t, int sub, uint32_t tid, int64_t* b, int64_t* si) const {
-    const uint32_t r = static_cast<uint32_t>(t.rt * 128 + sub * 16 + (tid >> 4));
-    const uint32_t c = t.cw * 16 + (tid & 15u);
-    if (r >= rows || c >= cb) return false;
-    *b = static_cast<int64_t>(r) * cb + c;
-    *si = place(r & 127u, c & 15u, 4);  // byte within the chunk's tiles
-    return true;
   }
   // The chunk's tiles (rt, 4 cw .. 4 cw + 3) are consecutive in memory.
   __host__ __device__ void chunk_tiles(Tile t, int64_t* first_byte, int* ntiles) const {
@@ -328,6 +319,7 @@ __device__ __forceinline__ void prefetch_second(const uint16_t* __restrict__ x, 
 // workgroup's first chunk, loaded into LDS before the prologue (the pass has
 // no registers to spare for the row-major pass's early first-block load):
 // 16384 x 8192 swizzled step 101.3 -> 100.65 us, three A/B pairs.
+template <int NT>
 __device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x, int64_t nb,
                                                   SwizzledScales smap, Launch vis, bool head, uint4* pre) {
   (void)nb;
@@ -346,7 +338,7 @@ __device__ __forceinline__ void prefetch_first_sw(const uint16_t* __restrict__ x
   const uint32_t off = rr < rows_here && c < smap.cb ? (rr * smap.cb + c) * 32u : 0xFFFFFFE0u;
   const int w = threadIdx.x >> 6;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(pre + w * 64), 16, off, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(pre + kThreads + w * 64), 16, off + 16u, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(pre + NT + w * 64), 16, off + 16u, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- one block
@@ -509,7 +501,7 @@ __device__ __forceinline__ void quant_blocks_rm(const T* __restrict__ x, int64_t
 // (head.counters set), chunk 0 holds the maxima in its scale tiles and the
 // arrival counters in its first code rows; workgroup 0, whose last visit it
 // is, waits before starting it.
-template <typename T, bool ROTATE, bool FAST, typename SMAP, bool PRE>
+template <typename T, bool ROTATE, bool FAST, typename SMAP, bool PRE, int NT>
 __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb, float g, float rg,
                                              const float2* __restrict__ tab, uint8_t* q, uint8_t* s,
                                              SMAP smap, Launch vis, const HeadGuard& head, const uint4* pre) {
@@ -533,18 +525,20 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
     const int64_t tile_blocks = row0 * smap.cb;
     const auto rx = chunk_rsrc(x + tile_blocks * 16, rows_here * smap.cb * 16u * static_cast<uint32_t>(sizeof(T)));
     const auto rq = chunk_rsrc(q + tile_blocks * 8, rows_here * smap.cb * 8u);
-    for (uint32_t i = threadIdx.x; i < 512; i += kThreads) stage[i] = 0u;
+    for (uint32_t i = threadIdx.x; i < 512; i += NT) stage[i] = 0u;
     __syncthreads();
     const uint32_t c = tile.cw * 16 + (threadIdx.x & 15u);
+    // NT / 16 rows of 16 blocks per sub-iteration
+    constexpr int kSubs = 128 / (NT / 16);
 #pragma unroll 1
-    for (int sub = 0; sub < SMAP::kSub; ++sub) {
-      const uint32_t r = static_cast<uint32_t>(sub) * 16u + (threadIdx.x >> 4);  // row within the tile
+    for (int sub = 0; sub < kSubs; ++sub) {
+      const uint32_t r = static_cast<uint32_t>(sub) * (NT / 16) + (threadIdx.x >> 4);  // row within the tile
       if (r >= rows_here || c >= smap.cb) continue;
       const uint32_t blk = r * smap.cb + c;
       float lo[8], hi[8];
       if (PRE && it == static_cast<int32_t>(mine) - 1 && sub == 0) {
         widen8(pre[threadIdx.x], lo);
-        widen8(pre[kThreads + threadIdx.x], hi);
+        widen8(pre[NT + threadIdx.x], hi);
       } else {
         Block<T> bl;
         bl.load_at(rx, blk);
@@ -562,7 +556,7 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
     int ntiles;
     smap.chunk_tiles(tile, &first, &ntiles);
     uint32_t* dst = reinterpret_cast<uint32_t*>(s + first);
-    for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += kThreads)
+    for (uint32_t i = threadIdx.x; i < static_cast<uint32_t>(ntiles) * 128u; i += NT)
       dst[i] = stage[i];
     __syncthreads();
   }
@@ -575,13 +569,16 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
 // arrival counters at `counters`; amax_out receives their maximum.  q and s carry no
 // __restrict__: the head is read and counted on through amax_src and later
 // overwritten through q or s.
-// Eight workgroups per CU (the grid size assumes it): at most 64 VGPRs.
-template <typename T, bool ROTATE, typename SMAP, AmaxMode MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(
+// Eight waves per SIMD (the grid size assumes it): at most 64 VGPRs.  NT: the
+// workgroup size, kThreads, or for swizzled scales also 1024 (small tensors:
+// a chunk's 128 rows in 2 sub-iterations instead of 8).
+template <typename T, bool ROTATE, typename SMAP, AmaxMode MODE, int NT = kThreads>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(
     const T* __restrict__ x, int64_t nb, uint32_t* amax_src, int npartials, Counters counters, float* amax_out,
     uint64_t head_ticks, uint8_t* q, uint8_t* s, float* gscale_out, SMAP smap, Launch vis) {
   constexpr bool hd = MODE == kHead;
   constexpr bool kGuard = MODE == kGiven;
+  static_assert(NT == kThreads || (SMAP::kStaged && NT == 1024), "workgroup size");
   __shared__ float2 tab[128];
   // pass 1's maxima (at most kMaxPartials words, in the head's first 2 KiB:
   // two 16-byte loads per lane) are loaded before any block, by every wave
@@ -607,10 +604,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     first.load(x, c, valid, threadIdx.x);
   }
   constexpr bool kPre = sizeof(T) == 2;
-  __shared__ uint4 pre[kPre ? 2 : 1][kPre ? kThreads : 1];  // one element where unused
+  __shared__ uint4 pre[kPre ? 2 : 1][kPre ? NT : 1];  // one element where unused
   if constexpr (kPre) {
     if constexpr (SMAP::kStaged)
-      prefetch_first_sw(x, nb, smap, vis, hd, &pre[0][0]);
+      prefetch_first_sw<NT>(x, nb, smap, vis, hd, &pre[0][0]);
     else
       prefetch_second(x, nb, smap, vis, hd, &pre[0][0]);
   }
@@ -681,7 +678,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     // uniform across the grid: every workgroup reads the same amax
     if (vis.allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
       if constexpr (SMAP::kStaged)
-        quant_blocks<T, ROTATE, true, SMAP, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, &pre[0][0]);
+        quant_blocks<T, ROTATE, true, SMAP, kPre, NT>(x, nb, g, rg, tab, q, s, smap, vis, head, &pre[0][0]);
       else
         quant_blocks_rm<T, ROTATE, true, kGuard, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, flo, fhi, faz,
                                                       &pre[0][0]);
@@ -689,7 +686,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     }
   }
   if constexpr (SMAP::kStaged)
-    quant_blocks<T, ROTATE, false, SMAP, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, &pre[0][0]);
+    quant_blocks<T, ROTATE, false, SMAP, kPre, NT>(x, nb, g, rg, tab, q, s, smap, vis, head, &pre[0][0]);
   else
     quant_blocks_rm<T, ROTATE, false, kGuard, kPre>(x, nb, g, rg, tab, q, s, smap, vis, head, flo, fhi, faz,
                                                    &pre[0][0]);

@@ -444,21 +444,30 @@ def test_swizzled_dequant(nv, rows, cols):
         assert torch.equal(y, y_ref)
 
 
-def test_swizzled_launch_shape_invariance(nv, monkeypatch):
-    """Super-tile chunks handed out over any number of workgroups give the
-    same bytes (ragged tile edges included)."""
-    x = mixed_input(300, 4112, "bf16", seed=8)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swizzled_launch_shape_invariance(nv, monkeypatch, dtype):
+    """Super-tile chunks handed out over any number of workgroups, of 256 or
+    1024 threads, give the same bytes (ragged tile edges included), with the
+    maxima at the head and through the zeroed word."""
+    x = mixed_input(300, 4112, dtype, seed=8)
     xd = to_dev(x)
     ref = [t.clone() for t in nv.rotquant_swizzled(xd)]
     torch.cuda.synchronize()
     oq, os_, og, oa = oracle.quantize(x, True)
     assert np.array_equal(ref[1].cpu().numpy(), oracle.swizzle_scales(os_))
-    for wgs in (1, 3, 7, 64, 100000):
-        monkeypatch.setenv("NVFP4RQ_QUANT_WGS", str(wgs))
-        got = nv.rotquant_swizzled(xd)
-        torch.cuda.synchronize()
-        for r, g in zip(ref, got):
-            assert torch.equal(r, g), wgs
+    for threads in (256, 1024):
+        monkeypatch.setenv("NVFP4RQ_SWZ_THREADS", str(threads))
+        for zeroed in (False, True):
+            if zeroed:
+                monkeypatch.setenv("NVFP4RQ_ZEROED_AMAX", "1")
+            else:
+                monkeypatch.delenv("NVFP4RQ_ZEROED_AMAX", raising=False)
+            for wgs in (1, 3, 7, 64, 100000):
+                monkeypatch.setenv("NVFP4RQ_QUANT_WGS", str(wgs))
+                got = nv.rotquant_swizzled(xd)
+                torch.cuda.synchronize()
+                for r, g in zip(ref, got):
+                    assert torch.equal(r, g), (threads, zeroed, wgs)
 
 
 # ---------------------------------------------------------------- pass-1 partials in q_out

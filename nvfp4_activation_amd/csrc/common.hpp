@@ -85,16 +85,40 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
   return u;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t u) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xF, 0xF, false));
+}
+
+// Wave maximum as a wave-uniform (scalar) value: each row of 16 lanes by DPP
+// exchanges (quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row
+// mirrors), then the four rows through readlane.  No LDS round trips.  Every
+// lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t u) {
+  u = umax(u, dpp_u32<0xB1>(u));
+  u = umax(u, dpp_u32<0x4E>(u));
+  u = umax(u, dpp_u32<0x141>(u));
+  u = umax(u, dpp_u32<0x140>(u));
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 0));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 16));
+  const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 32));
+  const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 48));
+  return umax(umax(r0, r1), umax(r2, r3));
+}
+
 // Workgroup maximum, then either one atomicMax per workgroup on a zeroed word
 // (partials == 0), or a plain store of the workgroup's maximum to out[wg]
 // (partials == 1; workgroup 0 also clears the arrival counters the quantize
-// pass uses, so no word has to be zeroed beforehand).  Non-negative binary32
-// values order like their bit patterns, so the maximum is exact and the same
-// for any reduction order (a NaN input stays visible as bits above +inf).
+// pass uses, so no word has to be zeroed beforehand, and the words from
+// out[grid] to out[kMaxPartials - 1], so that the quantize pass reduces all
+// kMaxPartials words without masking).  Non-negative binary32 values order
+// like their bit patterns, so the maximum is exact and the same for any
+// reduction order (a NaN input stays visible as bits above +inf).  Every
+// thread of the workgroup must call it.
 __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restrict__ out,
                                                  int partials, Counters counters) {
   __shared__ uint32_t part[kThreads / 64];
-  m = wave_max_u32(m);
+  m = wave_max_u32_uniform(m);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -106,7 +130,10 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restric
     else
       atomicMax(out, r);
   }
-  if (partials && blockIdx.x == 0 && threadIdx.x < kCounters) *counters.at(threadIdx.x) = 0u;
+  if (partials && blockIdx.x == 0) {
+    if (threadIdx.x < kCounters) *counters.at(threadIdx.x) = 0u;
+    for (uint32_t i = gridDim.x + threadIdx.x; i < static_cast<uint32_t>(kMaxPartials); i += kThreads) out[i] = 0u;
+  }
 }
 
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }

@@ -283,12 +283,12 @@ uint64_t head_ticks() {
 
 // Pass 2.  MODE kWord / kGiven: the amax is the word at amax_src (written by
 // pass 1 on the same tensor, or kept from elsewhere).  kHead: amax_src holds
-// npartials per-workgroup maxima (at the head of q or s), the arrival
+// pass 1's per-workgroup maxima (at the head of q or s), the arrival
 // counters are at `counters`, and the kernel writes the maxima's maximum to
 // amax_out.
 template <typename T, AmaxMode MODE, typename SMAP = RowMajorScales>
-nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_src, int npartials,
-                           Counters counters, float* amax_out, uint8_t* q, uint8_t* s, float* g, hipStream_t st,
+nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_src, Counters counters,
+                           float* amax_out, uint8_t* q, uint8_t* s, float* g, hipStream_t st,
                            SMAP smap = SMAP{}) {
   const int allow_fast = env_int("NVFP4RQ_EXACT_ONLY") ? 0 : 1;
   const int64_t nchunks = smap.chunks(nb);
@@ -325,15 +325,15 @@ nvfp4_status enqueue_quant(const T* x, int64_t nb, int rotate, uint32_t* amax_sr
     const int64_t forced = env_int("NVFP4RQ_SWZ_THREADS");
     if (forced ? forced == 1024 : nchunks <= 2LL * device_cus()) {
       e = rotate ? launch(rotquant_kernel<T, true, SMAP, MODE, 1024>, grid, dim3(1024), st, x, nb, amax_src,
-                          npartials, counters, amax_out, ticks, q, s, g, smap, vis)
+                          counters, amax_out, ticks, q, s, g, smap, vis)
                  : launch(rotquant_kernel<T, false, SMAP, MODE, 1024>, grid, dim3(1024), st, x, nb, amax_src,
-                          npartials, counters, amax_out, ticks, q, s, g, smap, vis);
+                          counters, amax_out, ticks, q, s, g, smap, vis);
       return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
     }
   }
-  e = rotate ? launch(rotquant_kernel<T, true, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src, npartials,
+  e = rotate ? launch(rotquant_kernel<T, true, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
                       counters, amax_out, ticks, q, s, g, smap, vis)
-             : launch(rotquant_kernel<T, false, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src, npartials,
+             : launch(rotquant_kernel<T, false, SMAP, MODE>, grid, dim3(kThreads), st, x, nb, amax_src,
                       counters, amax_out, ticks, q, s, g, smap, vis);
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
@@ -385,11 +385,11 @@ nvfp4_status enqueue_both(const T* x, int64_t nb, int rotate, uint8_t* q, uint8_
   if (nb == 0 || !head.partials || zeroed_word_path(g1, large)) {
     nvfp4_status r = enqueue_rotamax(x, nb, rotate, amax, st);
     if (r != NVFP4_OK) return r;
-    return enqueue_quant<T, kWord>(x, nb, rotate, reinterpret_cast<uint32_t*>(amax), 0, Counters{nullptr, 0u},
+    return enqueue_quant<T, kWord>(x, nb, rotate, reinterpret_cast<uint32_t*>(amax), Counters{nullptr, 0u},
                                    amax, q, s, g, st, smap);
   }
   if (launch_rotamax(x, nb, rotate, head.partials, 1, st, head.counters) != hipSuccess) return NVFP4_ERR_HIP;
-  return enqueue_quant<T, kHead>(x, nb, rotate, head.partials, g1, head.counters, amax, q, s, g, st, smap);
+  return enqueue_quant<T, kHead>(x, nb, rotate, head.partials, head.counters, amax, q, s, g, st, smap);
 }
 
 // Measurement support (calibrate.hpp): the fused call's launch sequence for
@@ -502,7 +502,7 @@ nvfp4_status quant_from_amax(const T* x, int64_t rows, int64_t cols, int rotate,
   // the amax word is only read (the kernel writes through amax_src on the
   // per-workgroup-maxima path alone)
   return enqueue_quant<T, kGiven>(x, nb, rotate,
-                                  const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(amax)), 0,
+                                  const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(amax)),
                                   Counters{nullptr, 0u}, nullptr, q, s, g, st);
 }
 

@@ -125,12 +125,15 @@ __device__ __forceinline__ float div_corrected(float y, float d, float r) {
   return __builtin_fmaf(e, r, q0);
 }
 
-// Two-word reciprocal of D: rh = RN(1/D) and rl = RN((1 - rh D) / D), the
-// residual 1 - rh D being exact as one fused multiply-add.  rh + rl is 1/D
-// within 2^-47 relative.
-__device__ __forceinline__ float2 recip2(float d) {
+// Two-word reciprocal of D: rh = RN(1/D) and rl = RN(e / D) with the
+// residual e = 1 - rh D, exact as one fused multiply-add.  rh + rl is 1/D
+// within 2^-47 relative.  rh is a correctly rounded division; rl comes from
+// the corrected product div_corrected(e, D, rh), which equals the correctly
+// rounded e / D for every binary32 D in [2^-60, 2^16), the range of the
+// kernels' tables (enumerated on the CPU, tests/helpers/fastdiv.c).
+__device__ __forceinline__ float2 recip2_corrected(float d) {
   const float rh = 1.0f / d;
-  return make_float2(rh, __builtin_fmaf(-rh, d, 1.0f) / d);
+  return make_float2(rh, div_corrected(__builtin_fmaf(-rh, d, 1.0f), d, rh));
 }
 
 // z / D from its two-word reciprocal (rh, rl): p = RN(z rl + 0),
@@ -211,6 +214,16 @@ __device__ __forceinline__ float2 e2m1_pair(uint32_t w) {
 __device__ __forceinline__ float global_scale(float amax) {
   const float g = (amax / 6.0f) / 448.0f;
   return g == 0.0f ? 1.0f : g;
+}
+
+// The same two divisions as corrected products, for amax in [2^-38, 2^15)
+// (the kernels' fast path): a / 6 gives the correctly rounded quotient for
+// every a >= 2^-124, and y / 448 for every y in [2^-41, 2^13), which holds
+// every y = RN(amax / 6) here (both enumerated over every binary32 in range,
+// tests/helpers/fastdiv.c); the result is never zero there.
+constexpr float kRecip448 = 1.0f / 448.0f;
+__device__ __forceinline__ float global_scale_corrected(float amax) {
+  return div_corrected(div_corrected(amax, 6.0f, kRecip6), 448.0f, kRecip448);
 }
 
 }  // namespace nvfp4rq

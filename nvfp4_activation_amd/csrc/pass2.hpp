@@ -565,8 +565,9 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
 // ---------------------------------------------------------------- kernel
 
 // amax_src: the amax word (kWord, kGiven) or pass 1's per-workgroup maxima
-// at the head of q (row-major) or s (swizzled): npartials of them, with the
-// arrival counters at `counters`; amax_out receives their maximum.  q and s carry no
+// at the head of q (row-major) or s (swizzled): kMaxPartials words, those
+// past pass 1's grid cleared, with the arrival counters at `counters`;
+// amax_out receives their maximum.  q and s carry no
 // __restrict__: the head is read and counted on through amax_src and later
 // overwritten through q or s.
 // Eight waves per SIMD (the grid size assumes it): at most 64 VGPRs.  NT: the
@@ -574,17 +575,17 @@ __device__ __forceinline__ void quant_blocks(const T* __restrict__ x, int64_t nb
 // a chunk's 128 rows in 2 sub-iterations instead of 8).
 template <typename T, bool ROTATE, typename SMAP, AmaxMode MODE, int NT = kThreads>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void rotquant_kernel(
-    const T* __restrict__ x, int64_t nb, uint32_t* amax_src, int npartials, Counters counters, float* amax_out,
+    const T* __restrict__ x, int64_t nb, uint32_t* amax_src, Counters counters, float* amax_out,
     uint64_t head_ticks, uint8_t* q, uint8_t* s, float* gscale_out, SMAP smap, Launch vis) {
   constexpr bool hd = MODE == kHead;
   constexpr bool kGuard = MODE == kGiven;
   static_assert(NT == kThreads || (SMAP::kStaged && NT == 1024), "workgroup size");
   __shared__ float2 tab[128];
-  // pass 1's maxima (at most kMaxPartials words, in the head's first 2 KiB:
-  // two 16-byte loads per lane) are loaded before any block, by every wave
-  // although only wave 0 reduces them: with no branch between these loads and
-  // their use, wave 0's wait for them leaves the block loads and the LDS
-  // prefetch below in flight (loads complete in issue order).
+  // pass 1's maxima (kMaxPartials words in the head's first 2 KiB, those
+  // past its grid cleared by pass 1: two 16-byte loads per lane) are loaded
+  // first, by every wave: with no branch between these loads and their use,
+  // a wave's wait for them leaves the block loads and the LDS prefetch below
+  // in flight (loads complete in issue order).
   u32x4 part0 = {0u, 0u, 0u, 0u}, part1 = {0u, 0u, 0u, 0u};
   if constexpr (hd) {
     const u32x4* p4 = reinterpret_cast<const u32x4*>(amax_src);
@@ -611,29 +612,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void ro
     else
       prefetch_second(x, nb, smap, vis, hd, &pre[0][0]);
   }
-  // Prologue.  Wave 0 alone derives the scalars: the global amax (reducing
-  // pass 1's maxima, then counting the workgroup in, or reading the word),
-  // g = (A / 6) / 448, 1/g and, on the fast path, the 128 two-word
-  // reciprocals; meanwhile every wave rotates its first block, which needs
-  // no scale.  One barrier then hands the scalars to all waves.
+  // Prologue.  Wave 0 alone derives the scalars: the global amax (pass 1's
+  // maxima reduced across the wave, then counted in, or the word), g =
+  // (A / 6) / 448 and, on the fast path, 1/g and the 128 two-word reciprocals
+  // (two entries per lane; entry 0, a constant, leaves lane 0's first slot
+  // to 1/g, through the same correctly rounded division); meanwhile every
+  // wave rotates its first block, which needs no scale.  One barrier then
+  // hands the scalars to all waves.  (Deriving them in every wave instead,
+  // each with a quarter of the table: 4096 x 4096 pass 2 8.0 against 7.7 us;
+  // the waves' extra work costs more than the shorter chain saves.)
   __shared__ uint32_t sh_abits;
   __shared__ float sh_g, sh_rg;
   if (threadIdx.x < 64) {
     uint32_t abits;
     if constexpr (hd) {
-      // words past npartials (other bytes of the output) masked out
-      const u32x4 v0 = part0, v1 = part1;
-      uint32_t m = 0u;
-      const int w0 = 4 * static_cast<int>(threadIdx.x), w1 = 256 + w0;
-      m = umax(m, w0 + 0 < npartials ? v0.x : 0u);
-      m = umax(m, w0 + 1 < npartials ? v0.y : 0u);
-      m = umax(m, w0 + 2 < npartials ? v0.z : 0u);
-      m = umax(m, w0 + 3 < npartials ? v0.w : 0u);
-      m = umax(m, w1 + 0 < npartials ? v1.x : 0u);
-      m = umax(m, w1 + 1 < npartials ? v1.y : 0u);
-      m = umax(m, w1 + 2 < npartials ? v1.z : 0u);
-      m = umax(m, w1 + 3 < npartials ? v1.w : 0u);
-      abits = wave_max_u32(m);
+      // the words past pass 1's grid were cleared by pass 1: no mask
+      const uint32_t m = umax(umax(umax(part0.x, part0.y), umax(part0.z, part0.w)),
+                              umax(umax(part1.x, part1.y), umax(part1.z, part1.w)));
+      abits = wave_max_u32_uniform(m);
       // this workgroup's reads of the maxima are complete (their values met
       // in the reduction) before it counts itself in; a relaxed increment
       // needs no cache write-back
@@ -645,14 +641,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void ro
     } else {
       abits = *amax_src;
     }
-    const float g = global_scale(__uint_as_float(abits));
-    float rg = 0.0f;
+    float g, rg = 0.0f;
     if (sizeof(T) == 2 && vis.allow_fast && abits >= kFastAmaxLo && abits < kFastAmaxHi) {
-      rg = 1.0f / g;
-      for (uint32_t k = threadIdx.x; k < 128; k += 64) {
-        const float sf = e4m3_value(k) * g;
-        tab[k] = recip2((ROTATE ? 4.0f : 1.0f) * (sf == 0.0f ? 1.0f : sf));
-      }
+      g = global_scale_corrected(__uint_as_float(abits));
+      // entry k: D = 4 E4M3(k) g (rotated input; E4M3(k) g unrotated), never
+      // zero in this range except for k = 0, whose D is then 4 (or 1) and
+      // whose reciprocal is exactly (1/4, 0) (or (1, 0))
+      constexpr float kUnit = ROTATE ? 4.0f : 1.0f;
+      const uint32_t k0 = threadIdx.x, k1 = threadIdx.x + 64;
+      const float2 r0 = recip2_corrected(k0 == 0 ? g : kUnit * (e4m3_value(k0) * g));
+      const float2 r1 = recip2_corrected(kUnit * (e4m3_value(k1) * g));
+      rg = r0.x;  // lane 0's
+      tab[k0] = k0 == 0 ? make_float2(1.0f / kUnit, 0.0f) : r0;
+      tab[k1] = r1;
+    } else {
+      g = global_scale(__uint_as_float(abits));
     }
     if (threadIdx.x == 0) {
       sh_abits = abits;
@@ -661,10 +664,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void ro
       if (blockIdx.x == 0) *gscale_out = g;
     }
   }
-  // (4096 x 4096: pass 2 8.10 -> 7.47 us, step 19.08 -> 18.39 us against
-  // every wave deriving the scalars itself, four interleaved runs; the
-  // fused pass at 16384 x 8192 issues 8.96 instead of 9.64 VALU
-  // lane-instructions per element)
   float flo[8], fhi[8], faz = 0.0f;
   if constexpr (!SMAP::kStaged) {
     first.unpack(flo, fhi);

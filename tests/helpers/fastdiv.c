@@ -133,6 +133,31 @@ long long verify_div_const(float c, uint32_t lo, uint32_t hi, uint32_t *ex)
 }
 
 /*
+ * The global scale (a / 6) / 448 as two corrected products with the
+ * constants RN(1/6) and RN(1/448), against the two binary32 divisions, for
+ * every binary32 a in [lo, hi] (the kernels' fast path: [2^-38, 2^15)).
+ */
+long long verify_global_scale(uint32_t lo, uint32_t hi, uint32_t *ex)
+{
+    const float r6 = 1.0f / 6.0f, r448 = 1.0f / 448.0f;
+    long long bad = 0;
+    uint32_t b = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t u = lo; u <= (int64_t)hi; u++) {
+        float a = fbits((uint32_t)u);
+        float want = (a / 6.0f) / 448.0f;
+        float got = mk(mk(a, 6.0f, r6), 448.0f, r448);
+        if (bitsf(want) != bitsf(got)) {
+            bad++;
+#pragma omp critical
+            b = (uint32_t)u;
+        }
+    }
+    *ex = b;
+    return bad;
+}
+
+/*
  * Random pairs over the whole range the kernels allow (d in [2^-62, 2^15],
  * z = 4y a multiple of 2^-133 with |z| <= 6.5 d or arbitrary below d):
  * the E2M1 code from q1 (sign bit for a quotient below zero, -0 and +0 both
@@ -268,6 +293,39 @@ long long verify_element2(int w, uint32_t *ex_d, uint32_t *ex_z)
     }
     *ex_d = bd;
     *ex_z = bz;
+    return bad;
+}
+
+/*
+ * The tail rl = RN(e / D) of the two-word reciprocal by the corrected product
+ * instead of a division: e = RN(1 - rh D) (exact as one fma), then
+ * mk(e, D, rh).  Compared bit for bit with e / D for every significand of D in
+ * every binade from 2^lo_exp to 2^hi_exp (the kernels' tables hold
+ * D in [2^-60, 2^16)); returns the number of mismatches and stores one D.
+ * Scaling D by 2^k scales rh, rl and every step of mk by 2^-k and leaves e
+ * unchanged, so one binade decides all binades in which nothing underflows;
+ * enumerating the extreme binades as well checks that.
+ */
+long long verify_recip_tail(int lo_exp, int hi_exp, uint32_t *ex_d)
+{
+    long long bad = 0;
+    uint32_t bd = 0;
+    for (int ex = lo_exp; ex < hi_exp; ex++) {
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+        for (int64_t D = 0; D < (1 << 23); D++) {
+            float d = fbits((uint32_t)(ex + 127) << 23 | (uint32_t)D);
+            float rh = 1.0f / d;
+            float e = fmaf(-rh, d, 1.0f);
+            float want = e / d;
+            float got = mk(e, d, rh);
+            if (bitsf(want) != bitsf(got)) {
+                bad++;
+#pragma omp critical
+                bd = bitsf(d);
+            }
+        }
+    }
+    *ex_d = bd;
     return bad;
 }
 

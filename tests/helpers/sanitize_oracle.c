@@ -68,6 +68,8 @@ long long sweep_e4m3_range(uint32_t lo, uint32_t hi, uint32_t *first);
 long long sweep_e4m3_linear(uint32_t lo, uint32_t hi, uint32_t stride, uint32_t *first);
 long long verify_div_const(float c, uint32_t lo, uint32_t hi, uint32_t *ex);
 long long verify_random_codes2(int64_t n, uint64_t seed);
+long long verify_recip_tail(int lo_exp, int hi_exp, uint32_t *ex_d);
+long long verify_global_scale(uint32_t lo, uint32_t hi, uint32_t *ex);
 
 static int failures = 0;
 #define CHECK(c, ...)                                      \
@@ -197,6 +199,8 @@ int main(void)
     CHECK(verify_div_const(6.0f, 0x40000000u, 0x4003FFFFu, &first) == 0, "divide by 6 slice");
     CHECK(verify_div_const(24.0f, 0x40000000u, 0x4003FFFFu, &first) == 0, "divide by 24 slice");
     CHECK(verify_random_codes2(200000, 7) == 0, "two-word quotient sample");
+    CHECK(verify_recip_tail(0, 1, &first) == 0, "corrected reciprocal tail, one binade");
+    CHECK(verify_global_scale(0x3F800000u, 0x3F83FFFFu, &first) == 0, "global scale slice");
 
     /* generators and the oracle on their tensors */
     const int64_t shapes[][2] = {{1, 16}, {3, 48}, {5, 1024}, {17, 1040}, {2, 4096}, {0, 64}, {7, 32}};

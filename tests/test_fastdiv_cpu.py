@@ -9,7 +9,9 @@ multiplications with reciprocals computed once with true divisions:
   the correctly rounded quotient at every input that can change an E4M3 scale;
 - the element quotient: a two-word reciprocal (two fused multiply-adds per
   element), whose E2M1 code equals that of the correctly rounded quotient at
-  every input where the two could differ.
+  every input where the two could differ;
+- the global scale (amax / 6) / 448 and the reciprocal table's low words: the
+  same correction, equal to the divisions at every input the kernels give it.
 
 See tests/helpers/fastdiv.c for the arguments.
 """
@@ -47,6 +49,10 @@ def lib(tmp_path_factory):
     lib.verify_random_codes.argtypes = [ctypes.c_int64, ctypes.c_uint64,
                                         ctypes.POINTER(ctypes.c_double)]
     lib.verify_random_codes.restype = ctypes.c_longlong
+    lib.verify_recip_tail.argtypes = [ctypes.c_int, ctypes.c_int, u32p]
+    lib.verify_recip_tail.restype = ctypes.c_longlong
+    lib.verify_global_scale.argtypes = [ctypes.c_uint32, ctypes.c_uint32, u32p]
+    lib.verify_global_scale.restype = ctypes.c_longlong
     return lib
 
 
@@ -99,3 +105,28 @@ def test_element_codes_two_operation_quotient(lib):
 
 def test_random_element_codes_two_operation_quotient(lib):
     assert lib.verify_random_codes2(200_000_000, 777) == 0
+
+
+def test_corrected_reciprocal_tail_every_divisor(lib):
+    """The table's low word RN((1 - rh D) / D) from the corrected product
+    equals the division for every binary32 D in [2^-60, 2^16), every divisor
+    the tables can hold (all exponents enumerated, not only one binade)."""
+    a = ctypes.c_uint32()
+    bad = lib.verify_recip_tail(-60, 16, ctypes.byref(a))
+    assert bad == 0, f"{bad} mismatches, e.g. D={a.value:#010x}"
+
+
+def test_divide_by_448_on_the_fast_range(lib):
+    """y / 448 through the corrected product for every y in [2^-41, 2^13),
+    which holds every RN(amax / 6) of the fast path."""
+    a = ctypes.c_uint32()
+    bad = lib.verify_div_const(448.0, 0x2B000000, 0x45FFFFFF, ctypes.byref(a))
+    assert bad == 0, f"{bad} mismatches, e.g. bits {a.value:#010x}"
+
+
+def test_global_scale_every_fast_amax(lib):
+    """(amax / 6) / 448 as two corrected products equals the two divisions
+    for every binary32 amax in [2^-38, 2^15), the fast path's range."""
+    a = ctypes.c_uint32()
+    bad = lib.verify_global_scale(0x2C800000, 0x46FFFFFF, ctypes.byref(a))
+    assert bad == 0, f"{bad} mismatches, e.g. amax bits {a.value:#010x}"

@@ -499,6 +499,36 @@ def test_partials_path_equals_zeroed_word_path(nv, monkeypatch, dtype):
         compare(f"partials {dtype} grids {a_wgs}/{q_wgs}", x, True, got)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols,a_wgs", [(128, 1024, 0), (300, 4112, 0), (777, 2064, 3), (1000, 1040, 511)])
+def test_head_ignores_stale_output_bytes(nv, monkeypatch, dtype, rows, cols, a_wgs):
+    """The quantize pass reduces all 512 words of the head, so the words past
+    pass 1's grid must be cleared by pass 1: with q_out and s_out filled with
+    0xFF beforehand (stale words reading as 0xFFFFFFFF, above any amax), the
+    row-major and swizzled calls still equal the oracle, for the default
+    pass-1 grids (most words unused) and for forced grids of 3 and 511
+    workgroups (509 words unused, and 1)."""
+    if a_wgs:
+        monkeypatch.setenv("NVFP4RQ_AMAX_WGS", str(a_wgs))
+    x = mixed_input(rows, cols, dtype, seed=rows + cols + a_wgs)
+    xd = to_dev(x)
+    ref = oracle.quantize(x, True)
+    q = torch.full((rows, cols // 2), 0xFF, dtype=torch.uint8, device="cuda:0")
+    s = torch.full((rows, cols // 16), 0xFF, dtype=torch.uint8, device="cuda:0")
+    g = torch.full((1,), float("nan"), device="cuda:0")
+    a = torch.full((1,), float("nan"), device="cuda:0")
+    nv.rotquant(xd, out=(q, s, g, a))
+    torch.cuda.synchronize()
+    compare(f"stale row-major {dtype} {rows}x{cols} grid {a_wgs}", x, True, (q, s, g, a), ref)
+    qs, ss, gs, as_ = nv.rotquant_swizzled(xd)
+    q.fill_(0xFF)
+    ss.fill_(0xFF)
+    nv.rotquant_swizzled(xd, out=(q, ss, gs, as_))
+    torch.cuda.synchronize()
+    assert np.array_equal(ss.cpu().numpy(), oracle.swizzle_scales(ref[1]))
+    compare(f"stale swizzled {dtype} {rows}x{cols} grid {a_wgs}", x, True, (q, ref[1], gs, as_), ref)
+
+
 def test_head_wait_with_tiny_time_limit(nv, monkeypatch):
     """A head-wait limit of one microsecond: the wait either completes in time
     (output equal to the oracle) or gives up and marks the call with a NaN

@@ -397,6 +397,10 @@ def main() -> int:
     # bytes), timed like the step: the ceiling this byte mix reaches here.
     qc, sc = torch.empty_like(q), torch.empty_like(s)
     calib_ms = timed(lambda: nv.stream_calibrate(x, out=(qc, sc)))
+    # ... and the twin launched as one pass with a workgroup per chunk: the
+    # ceiling of the single passes (given-scale, MXFP4), which have no
+    # earlier pass to leave input in the caches.
+    calib1_ms = timed(lambda: nv.stream_calibrate_single(x, out=(qc, sc)))
     del qc, sc
 
     # Context: decode (codes + scales + g in, fp32 out, inverse rotation).
@@ -469,6 +473,13 @@ def main() -> int:
                         "ms": round(calib_ms, 5),
                         "gbs": round(nbytes["step"] / (calib_ms * 1e-3) / 1e9, 2),
                         "value_over_calibration": round(calib_ms / ms, 4)},
+        "single_pass_calibration": {"kind": "no-arithmetic twin of the quantize pass launched alone, a "
+                                            "workgroup per chunk (nvfp4_stream_calibrate_single): the "
+                                            "given-scale pass's launch shape and bytes",
+                                    "ms": round(calib1_ms, 5),
+                                    "gbs": round(nbytes["pass2"] / (calib1_ms * 1e-3) / 1e9, 2),
+                                    "given_scale_over_calibration": round(calib1_ms / gs, 4),
+                                    "mxfp4_over_calibration": round(calib1_ms / mx_ms, 4)},
         "mxfp4_single_pass": {"ms": round(mx_ms, 5), "bytes_per_elem": mx_bytes / n,
                               "gbs": round(mx_bytes / (mx_ms * 1e-3) / 1e9, 2)},
         "unfused_three_kernel": {"ms": round(unfused_ms, 5),

@@ -307,6 +307,20 @@ nvfp4_status nvfp4_stream_calibrate(const uint16_t *x_bf16, int64_t rows, int64_
 nvfp4_status nvfp4_stream_calibrate_f32(const float *x, int64_t rows, int64_t cols,
                                         uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
 
+/*
+ * Measurement support, not part of the method: the same twin kernel launched
+ * as a single pass with a workgroup per chunk, the launch shape of
+ * nvfp4_quant_from_amax (and of mxfp4_rotquant, whose byte mix differs by
+ * 1/32 B per element): 2 B read and 0.5625 B written per bf16 element, with
+ * no earlier pass to leave any of the input in the caches.  Timing it gives
+ * the ceiling of a single pass.  Arguments, outputs and errors as for
+ * nvfp4_stream_calibrate.
+ */
+nvfp4_status nvfp4_stream_calibrate_single(const uint16_t *x_bf16, int64_t rows, int64_t cols,
+                                           uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
+nvfp4_status nvfp4_stream_calibrate_single_f32(const float *x, int64_t rows, int64_t cols,
+                                               uint8_t *q_out, uint8_t *s_out, hipStream_t stream);
+
 /* Static English text for a status code; never NULL. */
 const char *nvfp4_status_string(nvfp4_status status);
 

@@ -23,7 +23,7 @@ __all__ = [
     "LIB_PATH", "Nvfp4Error", "rotquant", "rotamax", "quant_from_amax", "dequant",
     "status_string", "lib", "mx_rotquant", "mx_dequant",
     "rotate16", "rotate_matrix", "rotquant_timed", "rotquant_swizzled", "dequant_swizzled",
-    "swizzled_scale_bytes", "stream_calibrate",
+    "swizzled_scale_bytes", "stream_calibrate", "stream_calibrate_single",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,8 @@ _SIGS = {
     "mxfp4_dequant": [_p, _p, _i64, _i64, _int, _p, _p],
     "nvfp4_stream_calibrate": [_p, _i64, _i64, _p, _p, _p],
     "nvfp4_stream_calibrate_f32": [_p, _i64, _i64, _p, _p, _p],
+    "nvfp4_stream_calibrate_single": [_p, _i64, _i64, _p, _p, _p],
+    "nvfp4_stream_calibrate_single_f32": [_p, _i64, _i64, _p, _p, _p],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -378,6 +380,18 @@ def stream_calibrate(x: torch.Tensor, out: tuple | None = None, stream=None):
     """Measurement support: the fused call's launch sequence with no-arithmetic
     twins of its two kernels (same grids, access patterns and bytes).  Returns
     (q, s) holding meaningless bytes."""
+    return _calibrate("nvfp4_stream_calibrate", x, out, stream)
+
+
+@_on_device
+def stream_calibrate_single(x: torch.Tensor, out: tuple | None = None, stream=None):
+    """Measurement support: the no-arithmetic twin launched as one pass with a
+    workgroup per chunk (the given-scale pass's launch shape).  Returns (q, s)
+    holding meaningless bytes."""
+    return _calibrate("nvfp4_stream_calibrate_single", x, out, stream)
+
+
+def _calibrate(name: str, x: torch.Tensor, out, stream):
     rows, cols = _check_input(x)
     if out is None:
         q = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
@@ -386,6 +400,6 @@ def stream_calibrate(x: torch.Tensor, out: tuple | None = None, stream=None):
         q, s = out
     _buf(q, rows * cols // 2, torch.uint8, x.device, "q")
     _buf(s, rows * cols // 16, torch.uint8, x.device, "s")
-    fn = _variant(x, "nvfp4_stream_calibrate")
+    fn = _variant(x, name)
     _check(fn, getattr(lib, fn)(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(x.device, stream)))
     return q, s

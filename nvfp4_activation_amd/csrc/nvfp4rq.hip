@@ -406,10 +406,8 @@ hipError_t launch_stream_read(const float* x, int64_t nb, uint32_t* out, int par
 }
 
 template <typename T>
-nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
-                              hipStream_t st) {
-  int64_t nb = 0;
-  nvfp4_status r = check_shape(rows, cols, &nb);
+nvfp4_status check_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, int64_t* nb) {
+  nvfp4_status r = check_shape(rows, cols, nb);
   if (r != NVFP4_OK) return r;
   const int64_t n = rows * cols;
   if (n != 0 && (!x || !q || !s)) return NVFP4_ERR_NULL;
@@ -417,6 +415,15 @@ nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q
   const Range rx = range_of(x, n * static_cast<int64_t>(sizeof(T)));
   const Range rq = range_of(q, n / 2), rs = range_of(s, n / 16);
   if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return NVFP4_ERR_ARG;
+  return NVFP4_OK;
+}
+
+template <typename T>
+nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                              hipStream_t st) {
+  int64_t nb = 0;
+  const nvfp4_status r = check_calibrate(x, rows, cols, q, s, &nb);
+  if (r != NVFP4_OK) return r;
   if (nb == 0) return NVFP4_OK;
   const int g1 = amax_grid_for(x, nb);
   const bool large = nb * 16 * static_cast<int64_t>(sizeof(T)) >= kOneShotInputBytes;
@@ -437,6 +444,25 @@ nvfp4_status stream_calibrate(const T* x, int64_t rows, int64_t cols, uint8_t* q
       smap.xcd_order = nchunks % 32 == 0 && !env_int("NVFP4RQ_PLAIN_ORDER") ? 1 : 0;
   }
   if (!word_path && grid.x > nchunks - 1) grid.x = static_cast<unsigned>(nchunks - 1);
+  const Launch vis = Launch::make(static_cast<uint32_t>(nchunks), grid.x);
+  return launch(stream_rw_kernel<T>, grid, dim3(kThreads), st, x, nb, q, s, smap, vis) == hipSuccess
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
+
+// The twin of a single pass with the amax as one word (the given-scale pass,
+// MXFP4): one launch, a workgroup per chunk, chunks in reverse index order.
+template <typename T>
+nvfp4_status stream_calibrate_single(const T* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                                     hipStream_t st) {
+  int64_t nb = 0;
+  const nvfp4_status r = check_calibrate(x, rows, cols, q, s, &nb);
+  if (r != NVFP4_OK) return r;
+  if (nb == 0) return NVFP4_OK;
+  RowMajorScales smap{};
+  smap.mirror = 1;
+  const int64_t nchunks = smap.chunks(nb);
+  const dim3 grid(clamp_grid(nchunks, nchunks));
   const Launch vis = Launch::make(static_cast<uint32_t>(nchunks), grid.x);
   return launch(stream_rw_kernel<T>, grid, dim3(kThreads), st, x, nb, q, s, smap, vis) == hipSuccess
              ? NVFP4_OK
@@ -754,6 +780,16 @@ nvfp4_status nvfp4_stream_calibrate(const uint16_t* x_bf16, int64_t rows, int64_
 nvfp4_status nvfp4_stream_calibrate_f32(const float* x, int64_t rows, int64_t cols, uint8_t* q_out,
                                         uint8_t* s_out, hipStream_t stream) {
   return stream_calibrate(x, rows, cols, q_out, s_out, stream);
+}
+
+nvfp4_status nvfp4_stream_calibrate_single(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                                           uint8_t* q_out, uint8_t* s_out, hipStream_t stream) {
+  return stream_calibrate_single(x_bf16, rows, cols, q_out, s_out, stream);
+}
+
+nvfp4_status nvfp4_stream_calibrate_single_f32(const float* x, int64_t rows, int64_t cols, uint8_t* q_out,
+                                               uint8_t* s_out, hipStream_t stream) {
+  return stream_calibrate_single(x, rows, cols, q_out, s_out, stream);
 }
 
 const char* nvfp4_status_string(nvfp4_status status) {

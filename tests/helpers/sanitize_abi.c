@@ -281,6 +281,10 @@ static void other_entries(void)
     expect("stream_calibrate_f32", 4, 64, nvfp4_stream_calibrate_f32(xf, 4, 64, q, s, 0), VALID);
     expect("stream_calibrate", 4, 64, nvfp4_stream_calibrate(NULL, 4, 64, q, s, 0), NUL);
     expect("stream_calibrate", 4, 40, nvfp4_stream_calibrate(xb, 4, 40, q, s, 0), SHP);
+    expect("stream_calibrate_single", 4, 64, nvfp4_stream_calibrate_single(xb, 4, 64, q, s, 0), VALID);
+    expect("stream_calibrate_single_f32", 4, 64, nvfp4_stream_calibrate_single_f32(xf, 4, 64, q, s, 0), VALID);
+    expect("stream_calibrate_single", 4, 64, nvfp4_stream_calibrate_single(NULL, 4, 64, q, s, 0), NUL);
+    expect("stream_calibrate_single", 4, 40, nvfp4_stream_calibrate_single(xb, 4, 40, q, s, 0), SHP);
     expect("stream_calibrate", 4, 64, nvfp4_stream_calibrate(xb + 4, 4, 64, q, s, 0), ALN);
     expect("stream_calibrate", 4, 64, nvfp4_stream_calibrate(xb, 4, 64, (uint8_t *)xb, s, 0), ARG);
     expect("stream_calibrate", 16384, 8192, nvfp4_stream_calibrate(xb, 16384, 8192, q, s, 0), VALID);

@@ -47,7 +47,8 @@ def lib():
         getattr(lib, name).argtypes = [p, i64, i64, i, p, p, p, p, p, p, i, p]
     lib.nvfp4_swizzled_scale_bytes.argtypes = [i64, i64]
     lib.nvfp4_swizzled_scale_bytes.restype = i64
-    for name in ("nvfp4_stream_calibrate", "nvfp4_stream_calibrate_f32"):
+    for name in ("nvfp4_stream_calibrate", "nvfp4_stream_calibrate_f32", "nvfp4_stream_calibrate_single",
+                 "nvfp4_stream_calibrate_single_f32"):
         getattr(lib, name).argtypes = [p, i64, i64, p, p, p]
     lib.nvfp4_status_string.argtypes = [i]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
@@ -63,7 +64,8 @@ def test_header_declares_the_boundary():
                  "nvfp4_rotquant_swizzled_f32", "nvfp4_dequant_swizzled",
                  "nvfp4_swizzled_scale_bytes", "nvfp4_rotquant_timed",
                  "nvfp4_rotquant_f32_timed", "nvfp4_stream_calibrate",
-                 "nvfp4_stream_calibrate_f32", "nvfp4_rotate_matrix", "nvfp4_rotate_matrix_f32"):
+                 "nvfp4_stream_calibrate_f32", "nvfp4_stream_calibrate_single",
+                 "nvfp4_stream_calibrate_single_f32", "nvfp4_rotate_matrix", "nvfp4_rotate_matrix_f32"):
         assert must in names
 
 
@@ -136,7 +138,8 @@ def test_rotamax_validation(lib):
 
 
 def test_stream_calibrate_validation(lib):
-    for name in ("nvfp4_stream_calibrate", "nvfp4_stream_calibrate_f32"):
+    for name in ("nvfp4_stream_calibrate", "nvfp4_stream_calibrate_f32", "nvfp4_stream_calibrate_single",
+                 "nvfp4_stream_calibrate_single_f32"):
         f = getattr(lib, name)
         assert f(None, 4, 64, Q, S, None) == ERR_NULL
         assert f(X, 4, 64, None, S, None) == ERR_NULL

@@ -1,6 +1,7 @@
-"""The calibration entry point (measurement support): it runs on every launch
-path of the fused call (small tensors, per-workgroup maxima, inputs of
-512 MiB and more), leaves its input unchanged and writes nothing outside its
+"""The calibration entry points (measurement support): the fused call's twin
+runs on every launch path of the fused call (small tensors, per-workgroup
+maxima, inputs of 512 MiB and more), the single-pass twin with a workgroup
+per chunk; both leave their input unchanged and write nothing outside their
 two output buffers."""
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ def test_calibration_stays_in_its_buffers(nv, rows, cols, dtype):
     sf, s = guarded(n // 16)
     for _ in range(2):
         nv.stream_calibrate(x, out=(q, s))
+        nv.stream_calibrate_single(x, out=(q, s))
     torch.cuda.synchronize()
     after = x.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).sum(dtype=torch.int64)
     assert torch.equal(before, after)

@@ -34,7 +34,8 @@ constexpr int64_t kLastLevelKeep = 160LL << 20;  // bytes of input pass 1 leaves
 // can run a workgroup per chunk (see enqueue_both).
 constexpr int64_t kOneShotInputBytes = 512LL << 20;
 // When pass 1 leaves its per-workgroup maxima in the outputs (the head), they
-// sit at words [0, npartials), npartials <= kMaxPartials, and the quantize
+// sit at words [0, grid) of kMaxPartials (pass 1's grid is at most that, and
+// its workgroup 0 clears the words from grid on), and the quantize
 // pass's arrival counters are kCounters words on separate 128-byte lines
 // (thousands of increments of one word serialize, and a workgroup's loads
 // wait behind its own pending atomic).  Row-major scales: both in q_out, the
@@ -78,13 +79,6 @@ __host__ __device__ inline int64_t pass1_wg_of(int64_t b, int64_t grid) {
 }
 __device__ __forceinline__ int64_t pass1_wg() { return pass1_wg_of(blockIdx.x, gridDim.x); }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1)
-    u = umax(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), off, 64)));
-  return u;
-}
-
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t u) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xF, 0xF, false));
@@ -104,6 +98,17 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t u) {
   const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 32));
   const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 48));
   return umax(umax(r0, r1), umax(r2, r3));
+}
+
+// Sum of lanes 0..15 (the wave's first row) as a wave-uniform value: the same
+// DPP exchanges with additions, then readlane 0.  Every lane of the wave must
+// be active.
+__device__ __forceinline__ uint32_t row0_sum_u32(uint32_t u) {
+  u += dpp_u32<0xB1>(u);
+  u += dpp_u32<0x4E>(u);
+  u += dpp_u32<0x141>(u);
+  u += dpp_u32<0x140>(u);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 0));
 }
 
 // Workgroup maximum, then either one atomicMax per workgroup on a zeroed word

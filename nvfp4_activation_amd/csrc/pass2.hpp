@@ -178,7 +178,7 @@ struct HeadGuard {
 
 __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
   __shared__ int timed_out;
-  if (threadIdx.x < 64) {  // wave 0: one counter per lane (lanes past kCounters add 0)
+  if (threadIdx.x < 64) {  // wave 0: one counter per lane of its first row (lanes past kCounters add 0)
     const uint64_t t0 = static_cast<uint64_t>(wall_clock64());
     int late = 0;
     // Each poll reads a counter with a fetch-and-add of zero: an atomic,
@@ -193,13 +193,12 @@ __device__ __forceinline__ void wait_for_head(const HeadGuard& h) {
     uint32_t zero = 0u;
     __asm__ volatile("" : "+v"(zero));
     for (;;) {
-      uint32_t c = threadIdx.x < kCounters
-                       ? __hip_atomic_fetch_add(h.counters.at(threadIdx.x), zero, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)
-                       : 0u;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) c += static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64));
-      if (c >= h.need) break;
+      static_assert(kCounters == 16, "the counters fill the wave's first row");
+      const uint32_t c = threadIdx.x < kCounters
+                             ? __hip_atomic_fetch_add(h.counters.at(threadIdx.x), zero, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                             : 0u;
+      if (row0_sum_u32(c) >= h.need) break;
       if (static_cast<uint64_t>(wall_clock64()) - t0 > h.ticks) {
         late = 1;
         break;

@@ -42,8 +42,8 @@
  *     NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN and NVFP4_ERR_ARG mean no work was
  *     enqueued and no output was touched.  NVFP4_ERR_HIP means a launch was
  *     rejected by the runtime; earlier launches of the same call may already
- *     be enqueued, so the outputs are then undefined.  Faults inside kernels surface at the caller's
- *     next synchronisation, as usual for HIP.
+ *     be enqueued, so the outputs are then undefined.  Faults inside kernels
+ *     surface at the caller's next synchronisation, as usual for HIP.
  *   - Outputs must not overlap the input or each other (NVFP4_ERR_ARG).
  *   - Calls that share an output buffer must be ordered (same stream or
  *     explicit events): the amax word can be an atomic accumulator, and the

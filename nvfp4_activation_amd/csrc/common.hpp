@@ -137,7 +137,8 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* __restric
   }
   if (partials && blockIdx.x == 0) {
     if (threadIdx.x < kCounters) *counters.at(threadIdx.x) = 0u;
-    for (uint32_t i = gridDim.x + threadIdx.x; i < static_cast<uint32_t>(kMaxPartials); i += kThreads) out[i] = 0u;
+    for (uint32_t i = gridDim.x + threadIdx.x; i < static_cast<uint32_t>(kMaxPartials); i += kThreads)
+      out[i] = 0u;
   }
 }
 

@@ -1,6 +1,7 @@
 // GPU side of the instruction checks (test code): runs the library's own
-// conversion helpers (nvfp4rq_device.hpp) over ranges of binary32 bit
-// patterns so that the tests can compare every output with the CPU oracle.
+// conversion and division helpers (nvfp4rq_device.hpp) over ranges of
+// binary32 bit patterns so that the tests can compare every output with a CPU
+// computation.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -53,7 +54,33 @@ __global__ void values_kernel(float* __restrict__ e4m3, float* __restrict__ e2m1
   }
 }
 
+// the fast path's global scale (two corrected products) of amax base + i * stride
+__global__ void gscale_kernel(uint32_t base, uint32_t stride, uint32_t n, uint32_t* __restrict__ out) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = __float_as_uint(global_scale_corrected(__uint_as_float(base + i * stride)));
+}
+
+// the two words of the reciprocal table entry for D = base + i * stride
+__global__ void recip2_kernel(uint32_t base, uint32_t stride, uint32_t n, uint32_t* __restrict__ out) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float2 r = recip2_corrected(__uint_as_float(base + i * stride));
+  out[2 * i] = __float_as_uint(r.x);
+  out[2 * i + 1] = __float_as_uint(r.y);
+}
+
 extern "C" {
+// out: n words; base + (n - 1) * stride must not wrap (the caller checks)
+int probe_gscale(uint32_t base, uint32_t stride, uint32_t n, uint32_t* out, hipStream_t st) {
+  gscale_kernel<<<(n + 255) / 256, 256, 0, st>>>(base, stride, n, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+// out: 2 n words
+int probe_recip2(uint32_t base, uint32_t stride, uint32_t n, uint32_t* out, hipStream_t st) {
+  recip2_kernel<<<(n + 255) / 256, 256, 0, st>>>(base, stride, n, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 int probe_e2m1(uint32_t base, uint32_t n, uint8_t* out, hipStream_t st) {
   e2m1_kernel<<<(n + 255) / 256, 256, 0, st>>>(base, n, out);
   return hipGetLastError() == hipSuccess ? 0 : 1;

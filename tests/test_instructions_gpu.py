@@ -12,6 +12,11 @@ through the library's own device helpers, against the CPU oracle.
   (section 2, _round_e4m3; section 3).
 - Decode: v_cvt_scalef32_pk_f32_fp4 (scale 1.0) behind e2m1_pair, every byte
   at every byte position, against the grid table of section 1, bit for bit.
+- The quantize prologue's corrected products on the device (the CPU proofs
+  in tests/helpers/fastdiv.c assume an exactly rounded fused multiply-add):
+  the global scale (amax / 6) / 448 against two binary32 divisions, and the
+  reciprocal table's words rh = RN(1/D), rl = RN((1 - rh D) / D) against
+  binary32 divisions, over whole binades and a strided sample of the range.
 """
 from __future__ import annotations
 
@@ -36,6 +41,10 @@ def probe():
     lib = ctypes.CDLL(PROBE)
     for name in ("probe_e2m1", "probe_e4m3"):
         getattr(lib, name).argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("probe_gscale", "probe_recip2"):
+        getattr(lib, name).argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
                                        ctypes.c_void_p]
         getattr(lib, name).restype = ctypes.c_int
     lib.probe_pack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -110,3 +119,56 @@ def test_nibble_order_and_value_tables(probe):
     got = e2.cpu().numpy().reshape(4, 512)
     for pos in range(4):
         assert np.array_equal(got[pos].view(np.uint32), want.view(np.uint32)), pos
+
+
+def _strided(lo: int, hi: int, stride: int):
+    """(base, stride, count) covering bit patterns lo, lo + stride, ... <= hi."""
+    return lo, stride, (hi - lo) // stride + 1
+
+
+def _floats(base: int, stride: int, n: int) -> np.ndarray:
+    bits = np.uint64(base) + np.arange(n, dtype=np.uint64) * np.uint64(stride)
+    assert int(bits[-1]) < 1 << 32
+    return bits.astype(np.uint32).view(np.float32)
+
+
+# whole binades at both ends and in the middle, plus a stride-97 sample of the range
+GSCALE_CASES = [_strided(0x2C800000, 0x2CFFFFFF, 1), _strided(0x3F000000, 0x3F7FFFFF, 1),
+                _strided(0x46800000, 0x46FFFFFF, 1), _strided(0x2C800000, 0x46FFFFFF, 97)]
+RECIP_CASES = [_strided(0x21800000, 0x21FFFFFF, 1), _strided(0x3F800000, 0x3FFFFFFF, 1),
+               _strided(0x47000000, 0x477FFFFF, 1), _strided(0x21800000, 0x477FFFFF, 97)]
+
+
+@pytest.mark.parametrize("base,stride,n", GSCALE_CASES)
+def test_global_scale_corrected_products(probe, base, stride, n):
+    """amax in the fast path's range [2^-38, 2^15): the device's two corrected
+    products give the bits of fl(fl(amax / 6) / 448)."""
+    out = torch.empty(n, dtype=torch.int32, device="cuda:0")
+    assert probe.probe_gscale(base, stride, n, out.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    a = _floats(base, stride, n)
+    want = (a / np.float32(6.0)) / np.float32(448.0)
+    assert want.dtype == np.float32
+    got = out.cpu().numpy().view(np.uint32)
+    bad = np.nonzero(got != want.view(np.uint32))[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first amax bits {a[bad[0]].view(np.uint32):#010x}"
+
+
+@pytest.mark.parametrize("base,stride,n", RECIP_CASES)
+def test_reciprocal_table_words(probe, base, stride, n):
+    """D in [2^-60, 2^16), every divisor the tables can hold: the device's
+    rh is RN(1/D) and its rl, from the corrected product, is RN(e / D) with
+    e = 1 - rh D (exact in binary32)."""
+    out = torch.empty(2 * n, dtype=torch.int32, device="cuda:0")
+    assert probe.probe_recip2(base, stride, n, out.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    d = _floats(base, stride, n)
+    rh = np.float32(1.0) / d
+    e64 = 1.0 - rh.astype(np.float64) * d.astype(np.float64)   # exact: 48-bit product near 1
+    e = e64.astype(np.float32)
+    assert np.array_equal(e.astype(np.float64), e64)            # the residual fits binary32
+    rl = e / d
+    got = out.cpu().numpy().view(np.uint32).reshape(n, 2)
+    for col, want, name in ((0, rh, "rh"), (1, rl, "rl")):
+        bad = np.nonzero(got[:, col] != want.view(np.uint32))[0]
+        assert bad.size == 0, f"{name}: {bad.size} mismatches, first D bits {d[bad[0]].view(np.uint32):#010x}"

@@ -63,7 +63,8 @@ def mixed_input(rows, cols, dtype, seed, spread=2.0):
     return v.astype(np.float32).reshape(rows, cols)
 
 
-SHAPES = [(1, 32), (3, 96), (127, 32), (5, 1024), (300, 4128), (1000, 1056), (257, 8192)]
+SHAPES = [(1, 32), (3, 96), (127, 32), (5, 1024), (300, 4128), (1000, 1056), (257, 8192),
+          (65536, 32), (4099, 64)]
 
 
 @pytest.mark.parametrize("rows,cols", SHAPES)

@@ -66,7 +66,8 @@ def compare(tag, x_np, rotate, got, ref=None):
 
 # ---------------------------------------------------------------- small shapes
 
-SHAPES = [(1, 16), (3, 48), (127, 16), (5, 1024), (300, 4112), (1000, 1040), (257, 8192)]
+SHAPES = [(1, 16), (3, 48), (127, 16), (5, 1024), (300, 4112), (1000, 1040), (257, 8192),
+          (65536, 16), (4099, 32)]
 
 
 def mixed_input(rows, cols, dtype, seed):
@@ -391,7 +392,8 @@ def test_dequant_small_shapes(nv, rows, cols, rotate):
 # ---------------------------------------------------------------- swizzled scales
 
 SWZ_SHAPES = [(1, 16), (3, 48), (127, 16), (128, 64), (129, 80), (300, 4112), (257, 8192),
-              (1000, 4096), (2000, 8192)]   # the last two: 16-chunk runs per XCD, ragged last tile
+              (1000, 4096), (2000, 8192),   # these two: 16-chunk runs per XCD, ragged last tile
+              (65536, 16), (4099, 256)]     # one block per row; the head with a 3-row last row tile
 
 
 @pytest.mark.parametrize("rows,cols", SWZ_SHAPES)

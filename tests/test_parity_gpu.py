@@ -67,7 +67,7 @@ def compare(tag, x_np, rotate, got, ref=None):
 # ---------------------------------------------------------------- small shapes
 
 SHAPES = [(1, 16), (3, 48), (127, 16), (5, 1024), (300, 4112), (1000, 1040), (257, 8192),
-          (65536, 16), (4099, 32)]
+          (65536, 16), (4099, 32), (1, 1048576), (3, 262160)]
 
 
 def mixed_input(rows, cols, dtype, seed):
@@ -393,7 +393,8 @@ def test_dequant_small_shapes(nv, rows, cols, rotate):
 
 SWZ_SHAPES = [(1, 16), (3, 48), (127, 16), (128, 64), (129, 80), (300, 4112), (257, 8192),
               (1000, 4096), (2000, 8192),   # these two: 16-chunk runs per XCD, ragged last tile
-              (65536, 16), (4099, 256)]     # one block per row; the head with a 3-row last row tile
+              (65536, 16), (4099, 256),     # one block per row; the head with a 3-row last row tile
+              (1, 1048576)]                 # one row: 4096 one-row chunks
 
 
 @pytest.mark.parametrize("rows,cols", SWZ_SHAPES)

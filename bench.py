@@ -196,6 +196,9 @@ def main() -> int:
                     help="print the plain / Hadamard / random-orthogonal round-trip error table "
                          "(NVFP4 and MXFP4) for the page's section-5 cases and the synthetic "
                          "workloads instead of timing")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="time the workload's tensor with rotation off (only where the workload "
+                         "defines one: gauss_1pct_cols_4096x4096, silu_ties_32768x14336)")
     ap.add_argument("--study-rows", type=int, default=4096,
                     help="row cap for the synthetic workloads in --error-study")
     args = ap.parse_args()
@@ -224,7 +227,10 @@ def main() -> int:
         return 2
     WORKLOAD = args.workload
     ROWS, COLS = synth.WORKLOADS[WORKLOAD][:2]
-    ROTATE = True in synth.WORKLOADS[WORKLOAD][3]
+    if args.no_rotate and False not in synth.WORKLOADS[WORKLOAD][3]:
+        print(f"workload {WORKLOAD} has no rotation-off tensor", file=sys.stderr)
+        return 2
+    ROTATE = not args.no_rotate and True in synth.WORKLOADS[WORKLOAD][3]
     w = synth.make(WORKLOAD, rotate=ROTATE)
     if w.x.dtype == np.uint16:
         x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -414,8 +420,8 @@ def main() -> int:
     torch.cuda.synchronize()
     same = bool(torch.equal(q, q2) and torch.equal(s, s2) and torch.equal(g, g2))
 
-    traffic = load_traffic(n) if WORKLOAD == DEFAULT_WORKLOAD else None
-    valu = load_valu() if WORKLOAD == DEFAULT_WORKLOAD else None
+    traffic = load_traffic(n) if WORKLOAD == DEFAULT_WORKLOAD and ROTATE else None
+    valu = load_valu() if WORKLOAD == DEFAULT_WORKLOAD and ROTATE else None
     out = {
         "metric": f"rotate+NVFP4-quantize GB/s and % of HBM peak, {ROWS}x{COLS} {dname}, 1 GPU",
         "value": round(gbs, 2),

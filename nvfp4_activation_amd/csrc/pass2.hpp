@@ -582,9 +582,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void ro
   __shared__ float2 tab[128];
   // pass 1's maxima (kMaxPartials words in the head's first 2 KiB, those
   // past its grid cleared by pass 1: two 16-byte loads per lane) are loaded
-  // first, by every wave: with no branch between these loads and their use,
-  // a wave's wait for them leaves the block loads and the LDS prefetch below
-  // in flight (loads complete in issue order).
+  // first, by every wave although only wave 0 reduces them: with no branch
+  // between these loads and their use, wave 0's wait for them leaves the
+  // block loads and the LDS prefetch below in flight (loads complete in
+  // issue order).
   u32x4 part0 = {0u, 0u, 0u, 0u}, part1 = {0u, 0u, 0u, 0u};
   if constexpr (hd) {
     const u32x4* p4 = reinterpret_cast<const u32x4*>(amax_src);
